@@ -1,0 +1,146 @@
+/*
+ * mla_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4-compressed sparse-MLA decode library.
+ *
+ * What the library computes follows the page "Prime Inference: Fast, Reliable Serving for
+ * Frontier Open Models" (Prime Intellect):
+ *   - section "Making room for low-latency decode": each MLA cache row stores the 512-value
+ *     latent as 4-bit E2M1 values with one FP8 (E4M3) scale per 16 values, and the 64-value rope
+ *     part as FP8: 352 bytes per row instead of 576;
+ *   - section "Native NVFP4 sparse MLA decode kernel": decode attention reads the rows selected
+ *     by the sparse indexer, unpacks them on chip (no intermediate buffer in device memory), and
+ *     computes with FP16 operands and FP32 accumulation; one query token's rows are split across
+ *     cooperating workgroups whose partial results are merged; entries of -1 in the 2048-entry
+ *     index list are empty and are not loaded;
+ *   - section "Changing the layout to reduce fragmentation": the cache is paged in 64-token
+ *     blocks; a page may belong to a block-major multi-layer layout, hence the page byte stride.
+ *
+ * Row layout (352 bytes): bytes [0,256) element codes, element 2k in the low nibble of byte k;
+ * bytes [256,288) the E4M3 scale of group g (elements 16g..16g+15); bytes [288,352) the E4M3 rope
+ * values. Scale = E4M3(amax/6) rounded to nearest even and saturated at 448; element code =
+ * nearest E2M1 value of x/scale, ties to the even code, saturated at 6; a zero scale zeroes the
+ * magnitudes and keeps the signs.
+ *
+ * Addressing: physical slot p = page*64 + offset lives at byte page*page_stride_bytes +
+ * offset*352. Logical position j of request b lives at slot block_table[b*max_pages + j/64]*64 +
+ * j%64.
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library never frees,
+ *     allocates persistent memory, or synchronizes the stream. All work is enqueued on `stream`.
+ *   - Argument errors (null pointers, unsupported shapes, misalignment, a too-small workspace)
+ *     are detected on the host before any HIP call and returned as MLA_ERR_INVALID_ARG /
+ *     MLA_ERR_UNSUPPORTED / MLA_ERR_WORKSPACE; nothing is enqueued in that case.
+ *   - A failing kernel launch returns MLA_ERR_HIP. mla_last_error() gives a per-thread text.
+ *   - Content (index values, page ids, slots) is the caller's contract, but kernels never read or
+ *     write outside [kv_cache, kv_cache + cache_bytes): a row that would fall outside, a page id
+ *     that is negative, or a position beyond the block table is treated as an empty slot (not
+ *     loaded / not written).
+ *   - Inputs must be finite; queries must be representable in FP16 (|q| < 65504), since the
+ *     contractions use FP16 operands.
+ */
+#ifndef MLA_NVFP4_H
+#define MLA_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE = 3,
+  MLA_ERR_HIP = 4
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
+
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_ROW_BYTES 352
+#define MLA_PAGE_ROWS 64
+#define MLA_MAX_TOPK 2048
+
+/* Quantize-on-append (page section "Making room for low-latency decode": the latent is stored
+ * as NVFP4, the rope part as FP8).
+ *   latent        bf16 [n_rows, 512], row i at latent + i*latent_row_stride elements.
+ *   rope          bf16 [n_rows, 64],  row i at rope + i*rope_row_stride elements.
+ *   slot_mapping  int64 [n_rows]: destination physical slot of row i; -1 = skip the row.
+ *   kv_cache      byte buffer of cache_bytes bytes; page_stride_bytes >= 64*352 and a multiple
+ *                 of 16; kv_cache 16-byte aligned.
+ * Writes exactly the 352 bytes of each non-skipped row. n_rows == 0 is a no-op. Rows whose slot
+ * falls outside the cache are not written. Two rows with the same slot race (last writer wins). */
+mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride,
+                                     const void* rope, int64_t rope_row_stride,
+                                     const int64_t* slot_mapping, int64_t n_rows,
+                                     void* kv_cache, int64_t page_stride_bytes,
+                                     int64_t cache_bytes, hipStream_t stream);
+
+/* Bytes of workspace mla_sparse_decode / mla_dense_decode need for `num_splits` row splits of
+ * `num_tokens` (= B*q_len) query tokens with H heads: num_tokens*num_splits*H*(512+1)*4 rounded
+ * up to 256. Zero when num_splits <= 1 (no partials are kept). */
+size_t mla_decode_workspace_size(int32_t num_tokens, int32_t H, int32_t num_splits);
+
+/* Number of row splits mla_sparse_decode will use for this shape when `max_splits` = 0 (auto,
+ * sized so that the launch covers one wave of the 256 compute units), or min(max_splits, topk/32)
+ * otherwise. The caller sizes the workspace with this number. */
+int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk,
+                                     int32_t max_splits);
+
+/* Number of row splits mla_dense_decode uses: ceil(max_pages*64 / split_tokens). */
+int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens);
+
+/* Sparse decode (page section "Native NVFP4 sparse MLA decode kernel").
+ *   q          [B, q_len, H, 576] contiguous, bf16 or fp32 (q_dtype): absorbed queries, latent
+ *              part first (512), rope part last (64).
+ *   kv_cache   cache_bytes bytes of 352-byte rows in 64-row pages of page_stride_bytes.
+ *   block_table int32 [B, max_pages] physical page ids.
+ *   topk_idx   int32 [B, q_len, topk]: logical positions selected for each query token, shared
+ *              by all heads; -1 marks an empty entry, anywhere in the list. 1 <= topk <= 2048.
+ *   H          multiple of 16 (heads are processed in groups of up to 64).
+ *   softmax_scale  scores are softmax_scale * (q . [latent; rope]).
+ *   out        fp32 [B, q_len, H, 512]: softmax-weighted sum of the selected latents.
+ *   lse        fp32 [B, q_len, H] natural-log sum of exp(scores), or NULL. A token whose list is
+ *              empty gets out = 0 and lse = -inf.
+ *   num_splits row splits per token (from mla_sparse_decode_num_splits); > 1 needs a workspace
+ *              of mla_decode_workspace_size(B*q_len, H, num_splits) bytes, 256-byte aligned.
+ * Results are deterministic: partials are merged in split order. */
+mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype,
+                             const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* topk_idx, int32_t topk,
+                             int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                             int32_t num_splits, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense decode over the whole cache of each request (no indexer): query token t of request b
+ * attends to logical positions 0 .. seq_lens[b]-q_len+t (causal inside the step), split into
+ * chunks of split_tokens positions (a multiple of 32) merged by log-sum-exp.
+ *   seq_lens   int32 [B] device array; values above max_pages*64 are clamped.
+ *   Other arguments as mla_sparse_decode; num_splits from mla_dense_decode_num_splits. */
+mla_status mla_dense_decode(const void* q, mla_dtype q_dtype,
+                            const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                            int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                            int32_t split_tokens, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Test hook, off the hot path: decode the rows at `slots` (int64 [n]) into fp32 [n, 576]
+ * (latent then rope), through the same on-chip decoder the attention kernels use. Values are
+ * exact. Slots outside the cache produce zeros. */
+mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,
+                                     int64_t cache_bytes, const int64_t* slots, int64_t n,
+                                     float* out, hipStream_t stream);
+
+const char* mla_status_string(mla_status s);
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_NVFP4_H */

@@ -1,0 +1,17 @@
+"""NVFP4-compressed sparse-MLA decode for MI355X (gfx950).
+
+The computation lives in the HIP library ``libmla_nvfp4.so`` (C ABI in ``include/mla_nvfp4.h``);
+this package holds its build script, the ctypes binding and the seeded workload generators.
+"""
+
+from ._lib import (  # noqa: F401
+    MlaError,
+    load_library,
+    mla_decode_workspace_size,
+    mla_dense_decode,
+    mla_dense_decode_num_splits,
+    mla_nvfp4_dequantize_rows,
+    mla_nvfp4_quantize_append,
+    mla_sparse_decode,
+    mla_sparse_decode_num_splits,
+)

@@ -1,0 +1,256 @@
+"""ctypes binding of ``libmla_nvfp4.so`` (declared in ``include/mla_nvfp4.h``).
+
+Argument marshalling only: tensors are checked for dtype / device / layout and handed over as
+device pointers with torch's current HIP stream. Every step of the computation runs in the HIP
+library; if the library is missing this module raises instead of falling back to anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_nvfp4.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_BF16, MLA_FP32 = 0, 1
+ROW_BYTES = 352
+PAGE_ROWS = 64
+LATENT_DIM = 512
+QK_DIM = 576
+
+EXPORTED = [
+    "mla_nvfp4_quantize_append",
+    "mla_decode_workspace_size",
+    "mla_sparse_decode_num_splits",
+    "mla_dense_decode_num_splits",
+    "mla_sparse_decode",
+    "mla_dense_decode",
+    "mla_nvfp4_dequantize_rows",
+    "mla_status_string",
+    "mla_last_error",
+]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load and type the library (once). Raises FileNotFoundError if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m nvfp4_compressed_mla_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.mla_nvfp4_quantize_append.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp]
+    lib.mla_nvfp4_quantize_append.restype = ctypes.c_int
+    lib.mla_decode_workspace_size.argtypes = [i32, i32, i32]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_sparse_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    lib.mla_sparse_decode_num_splits.restype = i32
+    lib.mla_dense_decode_num_splits.argtypes = [i32, i32]
+    lib.mla_dense_decode_num_splits.restype = i32
+    lib.mla_sparse_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
+                                      i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.mla_sparse_decode.restype = ctypes.c_int
+    lib.mla_dense_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
+                                     f32, i32, i32, vp, vp, vp, sz, vp]
+    lib.mla_dense_decode.restype = ctypes.c_int
+    lib.mla_nvfp4_dequantize_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+    lib.mla_nvfp4_dequantize_rows.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return load_library().mla_status_string(s).decode()
+    except Exception:
+        return f"status {s}"
+
+
+def _check(status: int) -> None:
+    if status != MLA_OK:
+        raise MlaError(status, load_library().mla_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype=None, device=True):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ---- entry points (same names as the C ABI) --------------------------------------------------
+
+def mla_nvfp4_quantize_append(latent, rope, slot_mapping, kv_cache, page_stride_bytes, stream=None):
+    """Quantize bf16 latent [N,512] / rope [N,64] rows into the cache at ``slot_mapping`` (int64)."""
+    torch = _torch()
+    _require(latent, "latent", torch.bfloat16)
+    _require(rope, "rope", torch.bfloat16)
+    _require(slot_mapping, "slot_mapping", torch.int64)
+    _require(kv_cache, "kv_cache", torch.uint8)
+    if latent.dim() != 2 or latent.shape[1] != 512 or latent.stride(1) != 1:
+        raise ValueError("latent must be [N, 512] with unit inner stride")
+    if rope.dim() != 2 or rope.shape[1] != 64 or rope.stride(1) != 1 or rope.shape[0] != latent.shape[0]:
+        raise ValueError("rope must be [N, 64] with unit inner stride")
+    if not slot_mapping.is_contiguous() or slot_mapping.numel() != latent.shape[0]:
+        raise ValueError("slot_mapping must be contiguous [N]")
+    lib = load_library()
+    _check(lib.mla_nvfp4_quantize_append(
+        _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(slot_mapping),
+        latent.shape[0], _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(), _stream(stream)))
+
+
+def mla_decode_workspace_size(num_tokens: int, H: int, num_splits: int) -> int:
+    return int(load_library().mla_decode_workspace_size(num_tokens, H, num_splits))
+
+
+def mla_sparse_decode_num_splits(num_tokens: int, H: int, topk: int, max_splits: int = 0) -> int:
+    return int(load_library().mla_sparse_decode_num_splits(num_tokens, H, topk, max_splits))
+
+
+def mla_dense_decode_num_splits(max_pages: int, split_tokens: int) -> int:
+    return int(load_library().mla_dense_decode_num_splits(max_pages, split_tokens))
+
+
+def _q_dtype(q):
+    torch = _torch()
+    if q.dtype == torch.bfloat16:
+        return MLA_BF16
+    if q.dtype == torch.float32:
+        return MLA_FP32
+    raise ValueError("q must be bf16 or fp32")
+
+
+def _outputs(q, out, lse, want_lse):
+    torch = _torch()
+    B, q_len, H, _ = q.shape
+    if out is None:
+        out = torch.empty(B, q_len, H, LATENT_DIM, device=q.device, dtype=torch.float32)
+    if lse is None and want_lse:
+        lse = torch.empty(B, q_len, H, device=q.device, dtype=torch.float32)
+    _require(out, "out", torch.float32)
+    if not out.is_contiguous() or tuple(out.shape) != (B, q_len, H, LATENT_DIM):
+        raise ValueError("out must be contiguous fp32 [B, q_len, H, 512]")
+    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, q_len, H)):
+        raise ValueError("lse must be contiguous fp32 [B, q_len, H]")
+    return out, lse
+
+
+def _workspace(workspace, n_tokens, H, splits, device):
+    torch = _torch()
+    need = mla_decode_workspace_size(n_tokens, H, splits)
+    if need == 0:
+        return workspace, 0 if workspace is None else workspace.numel()
+    if workspace is None:
+        workspace = torch.empty(need, device=device, dtype=torch.uint8)
+    return workspace, workspace.numel()
+
+
+def mla_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,
+                      out=None, lse=None, num_splits: int = 0, workspace=None, want_lse=True,
+                      stream=None):
+    """Sparse decode; returns (out fp32 [B,q_len,H,512], lse fp32 [B,q_len,H] or None).
+
+    ``num_splits`` 0 picks the library's launch-shaping choice. ``workspace`` (uint8 device
+    tensor) may be passed to keep the call free of allocations (graph capture).
+    """
+    torch = _torch()
+    _require(q, "q")
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(topk_idx, "topk_idx", torch.int32)
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, q_len, H, 576]")
+    B, q_len, H, _ = q.shape
+    if topk_idx.dim() != 3 or tuple(topk_idx.shape[:2]) != (B, q_len) or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous int32 [B, q_len, topk]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    topk = topk_idx.shape[2]
+    splits = num_splits or mla_sparse_decode_num_splits(B * q_len, H, topk, 0)
+    out, lse = _outputs(q, out, lse, want_lse)
+    workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
+    lib = load_library()
+    _check(lib.mla_sparse_decode(
+        _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
+        _ptr(block_table), block_table.shape[1], _ptr(topk_idx), topk, B, q_len, H,
+        float(softmax_scale), splits, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return out, lse
+
+
+def mla_dense_decode(q, kv_cache, page_stride_bytes, block_table, seq_lens, softmax_scale,
+                     split_tokens: int = 4096, out=None, lse=None, workspace=None, want_lse=True,
+                     stream=None):
+    """Dense decode over positions 0..seq_len-q_len+t; returns (out, lse)."""
+    torch = _torch()
+    _require(q, "q")
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, q_len, H, 576]")
+    B, q_len, H, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    splits = mla_dense_decode_num_splits(block_table.shape[1], split_tokens)
+    out, lse = _outputs(q, out, lse, want_lse)
+    workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
+    lib = load_library()
+    _check(lib.mla_dense_decode(
+        _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, q_len, H,
+        float(softmax_scale), int(split_tokens), splits, _ptr(out), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def mla_nvfp4_dequantize_rows(kv_cache, page_stride_bytes, slots, stream=None):
+    """Decode the rows at ``slots`` (int64) into fp32 [n, 576] with the on-chip decoder."""
+    torch = _torch()
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(slots, "slots", torch.int64)
+    slots = slots.contiguous()
+    out = torch.empty(slots.numel(), QK_DIM, device=kv_cache.device, dtype=torch.float32)
+    lib = load_library()
+    _check(lib.mla_nvfp4_dequantize_rows(_ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
+                                         _ptr(slots), slots.numel(), _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,276 @@
+// C-ABI entry points: argument validation on the host, launch shaping, kernel launches.
+// Nothing here allocates device memory or synchronizes; every check runs before any HIP call.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mla_nvfp4.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_last_error[0] = '\0';
+    return MLA_OK;
+  }
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kComputeUnits = 256;                 // MI355X: 8 XCDs x 32 CUs
+constexpr int64_t kMaxCacheBytes = int64_t(1) << 36;   // row offsets kept in 16-byte units (u32)
+
+mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_bytes) {
+  if (!kv_cache) return fail(MLA_ERR_INVALID_ARG, "kv_cache is null");
+  if (!aligned(kv_cache, 16)) return fail(MLA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
+  if (page_stride < (int64_t)MLA_PAGE_ROWS * MLA_ROW_BYTES || page_stride % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_stride_bytes %lld must be >= 22528 and a multiple of 16",
+                (long long)page_stride);
+  if (cache_bytes < MLA_ROW_BYTES || cache_bytes > kMaxCacheBytes)
+    return fail(MLA_ERR_INVALID_ARG, "cache_bytes %lld out of range [352, 2^36]", (long long)cache_bytes);
+  return MLA_OK;
+}
+
+// One group of up to 64 heads per workgroup; the number of workgroups a single wave of the chip
+// holds depends on how many heads a group carries (register footprint).
+int waves_capacity(int32_t H) { return H >= 64 ? kComputeUnits : 2 * kComputeUnits; }
+
+size_t ws_bytes(int64_t T, int64_t H, int64_t S) {
+  if (S <= 1) return 0;
+  const size_t b = (size_t)(T * S * H * (MLA_LATENT_DIM + 1)) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+mla_status check_decode_common(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                               int64_t page_stride, int64_t cache_bytes,
+                               const int32_t* block_table, int32_t max_pages, int32_t B,
+                               int32_t q_len, int32_t H, float softmax_scale, int32_t num_splits,
+                               float* out, float* lse, void* workspace, size_t workspace_bytes) {
+  if (!q || !block_table || !out) return fail(MLA_ERR_INVALID_ARG, "null q / block_table / out");
+  if (q_dtype != MLA_BF16 && q_dtype != MLA_FP32) return fail(MLA_ERR_UNSUPPORTED, "q_dtype must be bf16 or fp32");
+  mla_status st = check_cache(kv_cache, page_stride, cache_bytes);
+  if (st != MLA_OK) return st;
+  if (B < 1 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B and q_len must be >= 1");
+  if (H < 16 || H % 16 != 0) return fail(MLA_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 16", H);
+  if (max_pages < 1) return fail(MLA_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if ((int64_t)max_pages * MLA_PAGE_ROWS > (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "max_pages too large");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(MLA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (num_splits < 1 || num_splits > 4096) return fail(MLA_ERR_INVALID_ARG, "num_splits %d out of range", num_splits);
+  const int64_t T = (int64_t)B * q_len;
+  if (T * num_splits * ((H + 63) / 64) > (int64_t)1 << 28) return fail(MLA_ERR_INVALID_ARG, "launch too large");
+  if (num_splits > 1) {
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
+    if (!aligned(workspace, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < ws_bytes(T, H, num_splits))
+      return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes,
+                  ws_bytes(T, H, num_splits));
+  }
+  return MLA_OK;
+}
+
+mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, hipStream_t stream) {
+  const int64_t T = (int64_t)a.B * a.q_len;
+  const int32_t full = H / 64, tail = (H % 64) / 16;
+  const int32_t S = a.n_split;
+  const int32_t T32 = (int32_t)T;
+  if (full > 0) {
+    a.hg_begin = 0;
+    a.n_hg = full;
+    a.total_items = T32 * full * S;
+    a.items_per_xcd = (a.total_items + 7) / 8;
+    hipError_t e = mla::launch_decode(a, 4, dense, stream);
+    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+  }
+  if (tail > 0) {
+    a.hg_begin = full;
+    a.n_hg = 1;
+    a.total_items = T32 * S;
+    a.items_per_xcd = (a.total_items + 7) / 8;
+    hipError_t e = mla::launch_decode(a, tail, dense, stream);
+    if (e != hipSuccess) return hip_status(e, "decode kernel launch (tail head group)");
+  }
+  if (S > 1) {
+    hipError_t e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
+    if (e != hipSuccess) return hip_status(e, "combine kernel launch");
+  }
+  return hip_status(hipSuccess, "");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error; }
+
+mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride,
+                                     const void* rope, int64_t rope_row_stride,
+                                     const int64_t* slot_mapping, int64_t n_rows, void* kv_cache,
+                                     int64_t page_stride_bytes, int64_t cache_bytes,
+                                     hipStream_t stream) {
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  mla_status st = check_cache(kv_cache, page_stride_bytes, cache_bytes);
+  if (st != MLA_OK) return st;
+  if (n_rows == 0) return hip_status(hipSuccess, "");
+  if (!latent || !rope || !slot_mapping) return fail(MLA_ERR_INVALID_ARG, "null latent / rope / slot_mapping");
+  if (!aligned(latent, 16) || latent_row_stride < MLA_LATENT_DIM || latent_row_stride % 8 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "latent must be 16-byte aligned with a row stride >= 512 and a multiple of 8");
+  if (!aligned(rope, 2) || rope_row_stride < MLA_ROPE_DIM)
+    return fail(MLA_ERR_INVALID_ARG, "rope must be 2-byte aligned with a row stride >= 64");
+  if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  return hip_status(mla::launch_quantize_append(latent, latent_row_stride, rope, rope_row_stride,
+                                                slot_mapping, n_rows, kv_cache, page_stride_bytes,
+                                                cache_bytes, stream),
+                    "quantize_append launch");
+}
+
+size_t mla_decode_workspace_size(int32_t num_tokens, int32_t H, int32_t num_splits) {
+  if (num_tokens < 1 || H < 1) return 0;
+  return ws_bytes(num_tokens, H, num_splits);
+}
+
+int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk, int32_t max_splits) {
+  if (num_tokens < 1 || H < 16 || topk < 1) return 1;
+  const int32_t cap_by_rows = topk >= 64 ? topk / 64 : 1;    // keep >= 64 rows per split
+  if (max_splits > 0) return max_splits < cap_by_rows ? max_splits : cap_by_rows;
+  const int64_t groups = (H + 63) / 64;
+  const int64_t items = (int64_t)num_tokens * groups;
+  const int64_t cap = waves_capacity(H);
+  // Smallest split count whose items fill ~90% of one wave of workgroups.
+  int64_t s = (cap * 9 / 10 + items - 1) / items;
+  if (s < 1) s = 1;
+  if (s > 16) s = 16;
+  if (s > cap_by_rows) s = cap_by_rows;
+  return (int32_t)s;
+}
+
+int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens) {
+  if (max_pages < 1 || split_tokens < 64) return 1;
+  const int64_t n = (int64_t)max_pages * MLA_PAGE_ROWS;
+  return (int32_t)((n + split_tokens - 1) / split_tokens);
+}
+
+mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                             int64_t page_stride_bytes, int64_t cache_bytes,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                             int32_t H, float softmax_scale, int32_t num_splits, float* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                                      block_table, max_pages, B, q_len, H, softmax_scale,
+                                      num_splits, out, lse, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!topk_idx) return fail(MLA_ERR_INVALID_ARG, "topk_idx is null");
+  if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
+  if (!aligned(topk_idx, 4) || !aligned(block_table, 4)) return fail(MLA_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  const int64_t T = (int64_t)B * q_len;
+  int32_t split_rows = (topk + num_splits - 1) / num_splits;
+  split_rows = (split_rows + 63) & ~63;
+  mla::DecodeArgs a{};
+  a.q = q;
+  a.q_fp32 = (q_dtype == MLA_FP32);
+  a.cache = (const uint8_t*)kv_cache;
+  a.page_stride = page_stride_bytes;
+  a.cache_bytes = cache_bytes;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.B = B;
+  a.q_len = q_len;
+  a.H = H;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.n_split = num_splits;
+  a.split_rows = split_rows;
+  a.out = out;
+  a.lse = lse;
+  if (num_splits > 1) {
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + T * num_splits * H * MLA_LATENT_DIM;
+  }
+  return run_decode(a, H, false, stream);
+}
+
+mla_status mla_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                            int64_t page_stride_bytes, int64_t cache_bytes,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                            int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                            int32_t split_tokens, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                                      block_table, max_pages, B, q_len, H, softmax_scale,
+                                      num_splits, out, lse, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!seq_lens) return fail(MLA_ERR_INVALID_ARG, "seq_lens is null");
+  if (split_tokens < 64 || split_tokens % 64 != 0 || split_tokens > mla::kMaxDensePages * MLA_PAGE_ROWS)
+    return fail(MLA_ERR_UNSUPPORTED, "split_tokens %d must be a multiple of 64 in [64, 8192]", split_tokens);
+  if (num_splits != mla_dense_decode_num_splits(max_pages, split_tokens))
+    return fail(MLA_ERR_INVALID_ARG, "num_splits %d != ceil(max_pages*64/split_tokens) = %d", num_splits,
+                mla_dense_decode_num_splits(max_pages, split_tokens));
+  const int64_t T = (int64_t)B * q_len;
+  mla::DecodeArgs a{};
+  a.q = q;
+  a.q_fp32 = (q_dtype == MLA_FP32);
+  a.cache = (const uint8_t*)kv_cache;
+  a.page_stride = page_stride_bytes;
+  a.cache_bytes = cache_bytes;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.q_len = q_len;
+  a.H = H;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.n_split = num_splits;
+  a.split_rows = split_tokens;
+  a.out = out;
+  a.lse = lse;
+  if (num_splits > 1) {
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + T * num_splits * H * MLA_LATENT_DIM;
+  }
+  return run_decode(a, H, true, stream);
+}
+
+mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,
+                                     int64_t cache_bytes, const int64_t* slots, int64_t n,
+                                     float* out, hipStream_t stream) {
+  mla_status st = check_cache(kv_cache, page_stride_bytes, cache_bytes);
+  if (st != MLA_OK) return st;
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return hip_status(hipSuccess, "");
+  if (!slots || !out) return fail(MLA_ERR_INVALID_ARG, "null slots / out");
+  if (!aligned(slots, 8) || !aligned(out, 4)) return fail(MLA_ERR_INVALID_ARG, "misaligned slots / out");
+  return hip_status(mla::launch_dequantize_rows(kv_cache, page_stride_bytes, cache_bytes, slots, n,
+                                                out, stream),
+                    "dequantize_rows launch");
+}
+
+}  // extern "C"

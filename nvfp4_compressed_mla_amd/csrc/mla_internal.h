@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Arguments of the fused decode kernel (one struct, passed by value).
+struct DecodeArgs {
+  const void* q;            // [T, H, 576] bf16 or fp32, T = B*q_len
+  int32_t q_fp32;
+  const uint8_t* cache;
+  int64_t page_stride;      // bytes
+  int64_t cache_bytes;
+  const int32_t* block_table;   // [B, max_pages]
+  int32_t max_pages;
+  const int32_t* seq_lens;      // [B] (dense)
+  const int32_t* topk_idx;      // [T, topk] (sparse)
+  int32_t topk;
+  int32_t B, q_len, H;
+  float scale_log2;         // softmax_scale * log2(e)
+  int32_t n_split;          // row splits per (token, head group)
+  int32_t split_rows;       // list entries (sparse) or positions (dense) per split, multiple of 64
+  int32_t hg_begin;         // first 64-head group handled by this launch
+  int32_t n_hg;             // head groups handled by this launch
+  int32_t total_items;      // T * n_hg * n_split
+  int32_t items_per_xcd;    // ceil(total_items / 8)
+  float* out;               // [T, H, 512] (n_split == 1)
+  float* lse;               // [T, H] or null (n_split == 1)
+  float* ws_o;              // [T, n_split, H, 512] partial outputs (n_split > 1)
+  float* ws_lse;            // [T, n_split, H] partial log-sum-exp (natural log)
+};
+
+constexpr int kMaxSplitRows = 2048;   // sparse rows per split held in LDS
+constexpr int kMaxDensePages = 128;   // dense pages per split held in LDS (8192 positions)
+
+hipError_t launch_quantize_append(const void* latent, int64_t latent_stride, const void* rope,
+                                  int64_t rope_stride, const int64_t* slots, int64_t n_rows,
+                                  void* cache, int64_t page_stride, int64_t cache_bytes,
+                                  hipStream_t stream);
+
+hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_t cache_bytes,
+                                  const int64_t* slots, int64_t n, float* out, hipStream_t stream);
+
+// nh = heads per group / 16 (1..4); dense selects implicit positions.
+hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream);
+
+hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const float* ws_o,
+                          const float* ws_lse, float* out, float* lse, hipStream_t stream);
+
+}  // namespace mla

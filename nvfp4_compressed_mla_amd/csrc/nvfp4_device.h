@@ -1,0 +1,120 @@
+// Device-side NVFP4 / E4M3 codec pieces for gfx950 (CDNA4).
+//
+// Formats: OCP OFP8 E4M3 (bias 7, max 448, no infinities) for the group scales and the rope
+// part; OCP MX FP4 E2M1 (values 0, .5, 1, 1.5, 2, 3, 4, 6) for the latent elements. Row format
+// from "Prime Inference: Fast, Reliable Serving for Frontier Open Models", section "Making room
+// for low-latency decode": 4-bit latent values with one FP8 scale per 16 values plus a 64-value
+// FP8 rope part, 352 bytes per row.
+//
+// Encoding is integer/compare arithmetic only, so it is bit-exact by construction:
+//   * E4M3 encode rounds the fp32 mantissa to 3 bits with round-half-even on the raw bits;
+//   * E2M1 encode compares |x| against the midpoints of the E2M1 grid times the scale
+//     (.25s .75s 1.25s 1.75s 2.5s 3.5s 5s), which are exact fp32 products, with the comparison
+//     sense at each midpoint chosen so that ties go to the even code.
+// Decoding to FP16 MFMA operands uses the gfx950 packed conversions with unit scale, then one
+// packed FP16 multiply by the group scale; every product e2m1 * e4m3 is exact in FP16
+// (at most 6 significant bits, magnitudes in [2^-10, 2688]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kQkDim = 576;
+constexpr int kRowBytes = 352;
+constexpr int kCodeBytes = 256;   // 512 4-bit codes
+constexpr int kScaleOff = 256;    // 32 E4M3 group scales
+constexpr int kRopeOff = 288;     // 64 E4M3 rope values
+constexpr int kPageRows = 64;
+
+// ---- encode --------------------------------------------------------------------------------
+
+// Nearest E4M3 byte of a finite fp32 value, ties to even, magnitudes >= 448 saturate to 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const float af = __uint_as_float(a);
+  uint32_t code;
+  if (af >= 448.0f) {
+    code = 0x7Eu;
+  } else if (af < 0.015625f) {            // below 2^-6: subnormal grid, step 2^-9
+    code = (uint32_t)__builtin_rintf(af * 512.0f);   // exact scaling, round half even; 8 -> 2^-6
+  } else {                                 // normal: keep 3 mantissa bits, round half even
+    const uint32_t e = (a >> 23) - 120u;   // E4M3 biased exponent (fp32 bias 127, E4M3 bias 7)
+    const uint32_t keep = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (keep & 1u));
+    code = ((e << 3) | keep) + up;         // a carry out of the mantissa bumps the exponent
+  }
+  return code | sign;
+}
+
+// Value of an E4M3 byte (finite codes).
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = (e == 0u) ? (float)m * (1.0f / 512.0f)
+                              : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// 4-bit E2M1 code of x against a decoded scale s >= 0 (s == 0: magnitude 0, sign kept).
+__device__ __forceinline__ uint32_t e2m1_encode(float x, float s) {
+  const float a = __builtin_fabsf(x);
+  uint32_t mag = (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) +
+                 (uint32_t)(a > 1.25f * s) + (uint32_t)(a >= 1.75f * s) +
+                 (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) + (uint32_t)(a > 5.0f * s);
+  mag = (s > 0.0f) ? mag : 0u;
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// ---- decode to FP16 operands ------------------------------------------------------------------
+
+// Two E2M1 codes in byte `sel` of w -> FP16 pair (low nibble first), unit scale.
+template <int SEL>
+__device__ __forceinline__ half2v fp4x2_to_half2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Two E4M3 bytes in 16-bit word `HI` of w -> FP16 pair (low byte first), unit scale.
+template <bool HI>
+__device__ __forceinline__ half2v fp8x2_to_half2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Eight E2M1 codes of one dword (8 consecutive elements of one group) times an FP16 scale pair
+// -> eight FP16 values in element order.
+__device__ __forceinline__ half8v decode_fp4x8(uint32_t w, half2v s2) {
+  const half2v p0 = fp4x2_to_half2<0>(w) * s2;
+  const half2v p1 = fp4x2_to_half2<1>(w) * s2;
+  const half2v p2 = fp4x2_to_half2<2>(w) * s2;
+  const half2v p3 = fp4x2_to_half2<3>(w) * s2;
+  return half8v{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Eight E4M3 bytes (two dwords) -> eight FP16 values in byte order.
+__device__ __forceinline__ half8v decode_fp8x8(uint32_t lo, uint32_t hi) {
+  const half2v p0 = fp8x2_to_half2<false>(lo);
+  const half2v p1 = fp8x2_to_half2<true>(lo);
+  const half2v p2 = fp8x2_to_half2<false>(hi);
+  const half2v p3 = fp8x2_to_half2<true>(hi);
+  return half8v{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// E4M3 scale byte -> FP16 pair (s, s).
+__device__ __forceinline__ half2v scale_pair(uint32_t b) {
+  const half2v s = fp8x2_to_half2<false>(b & 0xFFu);
+  return half2v{s[0], s[0]};
+}
+
+}  // namespace mla

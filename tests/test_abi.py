@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad arguments
+on the host before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_compressed_mla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)          # never dereferenced: validation fails first
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(mla_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mla_nvfp4_quantize_append", "mla_sparse_decode", "mla_dense_decode"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, q_dtype=0, cache=FAKE, stride=22528, cache_bytes=22528 * 4, bt=FAKE,
+             max_pages=4, idx=FAKE, topk=256, B=1, q_len=1, H=16, scale=0.04, splits=1,
+             out=FAKE, lse=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.mla_sparse_decode(a["q"], a["q_dtype"], a["cache"], a["stride"], a["cache_bytes"],
+                                 a["bt"], a["max_pages"], a["idx"], a["topk"], a["B"], a["q_len"],
+                                 a["H"], a["scale"], a["splits"], a["out"], a["lse"], a["ws"],
+                                 a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(cache=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(idx=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(q_dtype=7), UNSUPPORTED),
+    (dict(H=24), UNSUPPORTED),
+    (dict(H=0), UNSUPPORTED),
+    (dict(topk=0), UNSUPPORTED),
+    (dict(topk=2049), UNSUPPORTED),
+    (dict(stride=22528 - 16), INVALID),
+    (dict(stride=22528 + 8), INVALID),
+    (dict(cache=ctypes.c_void_p(0x10008)), INVALID),
+    (dict(cache_bytes=100), INVALID),
+    (dict(B=0), INVALID),
+    (dict(q_len=0), INVALID),
+    (dict(max_pages=0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(splits=0), INVALID),
+    (dict(splits=4), WORKSPACE),
+    (dict(splits=4, ws=ctypes.c_void_p(0x10040), ws_bytes=1 << 30), WORKSPACE),
+    (dict(splits=4, ws=FAKE, ws_bytes=100), WORKSPACE),
+])
+def test_sparse_decode_rejects(lib, kw, code):
+    assert _sparse(lib, **kw) == code
+    assert lib.mla_last_error().decode() != ""
+
+
+def test_dense_decode_rejects(lib):
+    def call(**kw):
+        a = dict(seq=FAKE, split=4096, splits=1, max_pages=4, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.mla_dense_decode(FAKE, 0, FAKE, 22528, 22528 * 4, FAKE, a["max_pages"], a["seq"],
+                                    1, 1, 64, 0.04, a["split"], a["splits"], FAKE, None, a["ws"],
+                                    a["ws_bytes"], None)
+    assert call(seq=None) == INVALID
+    assert call(split=100) == UNSUPPORTED
+    assert call(split=16384) == UNSUPPORTED
+    # must equal ceil(max_pages*64/split_tokens)
+    assert call(splits=2, ws=FAKE, ws_bytes=1 << 30) == INVALID
+    assert call(max_pages=200, split=4096, splits=4) == WORKSPACE
+
+
+def test_quantize_append_rejects(lib):
+    f = lib.mla_nvfp4_quantize_append
+    assert f(FAKE, 512, FAKE, 64, FAKE, 0, FAKE, 22528, 22528, None) == OK        # n_rows = 0: no-op
+    assert f(FAKE, 512, FAKE, 64, FAKE, -1, FAKE, 22528, 22528, None) == INVALID
+    assert f(None, 512, FAKE, 64, FAKE, 5, FAKE, 22528, 22528, None) == INVALID
+    assert f(FAKE, 500, FAKE, 64, FAKE, 5, FAKE, 22528, 22528, None) == INVALID
+    assert f(FAKE, 516, FAKE, 64, FAKE, 5, FAKE, 22528, 22528, None) == INVALID
+    assert f(FAKE, 512, FAKE, 32, FAKE, 5, FAKE, 22528, 22528, None) == INVALID
+    assert f(FAKE, 512, FAKE, 64, FAKE, 5, None, 22528, 22528, None) == INVALID
+    assert f(FAKE, 512, FAKE, 64, FAKE, 5, FAKE, 1000, 22528, None) == INVALID
+    assert f(ctypes.c_void_p(0x10002), 512, FAKE, 64, FAKE, 5, FAKE, 22528, 22528, None) == INVALID
+
+
+def test_dequantize_rows_rejects(lib):
+    f = lib.mla_nvfp4_dequantize_rows
+    assert f(FAKE, 22528, 22528, FAKE, 0, FAKE, None) == OK
+    assert f(None, 22528, 22528, FAKE, 3, FAKE, None) == INVALID
+    assert f(FAKE, 22528, 22528, None, 3, FAKE, None) == INVALID
+    assert f(FAKE, 22528, 22528, FAKE, -2, FAKE, None) == INVALID
+
+
+def test_launch_shaping(lib):
+    # one wave of 256 compute units at 64 heads per workgroup
+    assert lib.mla_sparse_decode_num_splits(32, 64, 2048, 0) == 8
+    assert lib.mla_sparse_decode_num_splits(240, 64, 2048, 0) == 1
+    assert lib.mla_sparse_decode_num_splits(1, 16, 256, 0) == 4        # >= 64 rows per split
+    assert lib.mla_sparse_decode_num_splits(1, 64, 2048, 100) == 32
+    assert lib.mla_dense_decode_num_splits(2336, 4096) == 37
+    assert lib.mla_decode_workspace_size(32, 64, 1) == 0
+    assert lib.mla_decode_workspace_size(32, 64, 8) == 32 * 8 * 64 * 513 * 4
+    assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
