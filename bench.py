@@ -1,0 +1,482 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the NVFP4-compressed sparse-MLA decode step on MI355X.
+
+Workload (the metric's configuration): B=32 requests, q_len=1, H=64 heads, each request a
+140K-token (143,360) NVFP4 cache in 64-row pages with random block tables, top-k 2048 positions per
+query token drawn uniformly without replacement, bf16 queries, fp32 output. A step is one pass of
+the hot path over one batch: quantize-append of the step's new rows (one per query token) and the
+sparse decode (index resolve, row gather, on-chip decode, QK, online softmax, PV, split combine).
+
+Inputs are synthetic and seeded, generated and quantized on the GPU before timing. To keep the
+256 MB Infinity Cache from serving the gathers, the timed steps rotate through R distinct
+(index list, query) sets whose gathered bytes total >= 1 GB. Steps run as replays of captured
+HIP graphs. The fused decode kernel's own duration is taken with HIP events recorded around it by
+the library (``mla_set_timing_events``) on the launch stream.
+
+``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PAGE = 64 * 352
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batched_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_compressed_mla_amd", "csrc", f)
+                  for f in ("decode.hip", "nvfp4_device.h")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---- workload construction ---------------------------------------------------------------------
+
+class SparseWorkload:
+    """Caches, tables, rotated queries / index lists and preallocated outputs of one config."""
+
+    def __init__(self, name, B, q_len, H, ctx, topk, append_rows, rotations, seed, device,
+                 q_lens=None, keep_latent=False):
+        import torch
+        from nvfp4_compressed_mla_amd import workloads as wl
+        import nvfp4_compressed_mla_amd as m
+        self.name, self.B, self.q_len, self.H, self.topk = name, B, q_len, H, topk
+        self.ctx = list(ctx)
+        self.append_rows = append_rows
+        self.q_lens = q_lens
+        existing = [c - append_rows for c in self.ctx]
+        total_rows = sum(existing)
+        # pages for the existing rows plus the rows this step appends
+        bt, n_pages = wl.gen_block_table(self.ctx, seed + 1, device)
+        self.block_table = bt
+        self.cache = torch.zeros(n_pages * PAGE, dtype=torch.uint8, device=device)
+        lat, rope = wl.gen_latent_rope(total_rows, seed, device)
+        slots = torch.cat([wl.slot_mapping_for(bt, b, 0, c) for b, c in enumerate(existing)])
+        m.mla_nvfp4_quantize_append(lat, rope, slots, self.cache, PAGE)
+        self.row_base = [0]
+        for c in existing[:-1]:
+            self.row_base.append(self.row_base[-1] + c)
+        self.latent, self.rope = (lat, rope) if keep_latent else (None, None)
+        # rows appended by every step: append_rows per request at positions [existing, ctx)
+        n_new = append_rows * B
+        self.new_lat, self.new_rope = wl.gen_latent_rope(n_new, seed + 7, device)
+        self.new_slots = torch.cat([wl.slot_mapping_for(bt, b, existing[b], append_rows)
+                                    for b in range(B)])
+        self.rot = rotations
+        self.q = [wl.gen_queries(B, q_len, H, "bf16", seed + 100 + r, device) for r in range(rotations)]
+        if q_lens is None and len(set(self.ctx)) == 1 and self.ctx[0] >= topk:
+            self.idx = [wl.gen_topk_batched(B, q_len, topk, self.ctx[0], seed + 200 + r, device)
+                        for r in range(rotations)]
+        else:
+            self.idx = [wl.gen_topk(B, q_len, topk, self.ctx, seed + 200 + r, device, q_lens=q_lens)
+                        for r in range(rotations)]
+        T = B * q_len
+        self.splits = m.mla_sparse_decode_num_splits(T, H, topk, 0)
+        ws = m.mla_decode_workspace_size(T, H, self.splits)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.out = torch.empty(B, q_len, H, 512, dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, q_len, H, dtype=torch.float32, device=device)
+        # algorithmic units: valid (token, row) pairs of each rotation
+        self.valid_pairs = [int((i >= 0).sum().item()) for i in self.idx]
+        torch.cuda.synchronize()
+
+    def decode(self, r):
+        import nvfp4_compressed_mla_amd as m
+        m.mla_sparse_decode(self.q[r], self.cache, PAGE, self.block_table, self.idx[r],
+                            1.0 / math.sqrt(576.0), out=self.out, lse=self.lse,
+                            num_splits=self.splits, workspace=self.ws)
+
+    def append(self):
+        import nvfp4_compressed_mla_amd as m
+        if self.append_rows:
+            m.mla_nvfp4_quantize_append(self.new_lat, self.new_rope, self.new_slots, self.cache, PAGE)
+
+    def step(self, r):
+        self.append()
+        self.decode(r)
+
+    # algorithmic bytes / flops of the fused decode kernel for rotation r
+    def kernel_bytes(self, r):
+        T = self.B * self.q_len
+        return self.valid_pairs[r] * (352 + 4 + 4) + T * self.H * 576 * 2
+
+    def gathered_bytes(self, r):
+        return self.valid_pairs[r] * 352
+
+    def flops(self, r):
+        return self.valid_pairs[r] * 2 * self.H * (576 + 512)
+
+    def step_bytes(self, r):
+        """Whole-step algorithmic bytes: append (bf16 in, 352 B out, slot) + decode incl. output."""
+        T = self.B * self.q_len
+        app = self.append_rows * self.B * (1152 + 352 + 8)
+        return app + self.kernel_bytes(r) + T * self.H * (512 + 1) * 4
+
+
+class DenseWorkload:
+    def __init__(self, B, H, ctx, split_tokens, rotations, seed, device):
+        import torch
+        from nvfp4_compressed_mla_amd import workloads as wl
+        import nvfp4_compressed_mla_amd as m
+        self.B, self.H, self.ctx, self.split_tokens = B, H, ctx, split_tokens
+        # `rotations` independent caches so consecutive launches stream different bytes
+        self.caches, self.tables = [], []
+        for r in range(rotations):
+            bt, n_pages = wl.gen_block_table([ctx] * B, seed + 1 + r, device)
+            cache = torch.zeros(n_pages * PAGE, dtype=torch.uint8, device=device)
+            lat, rope = wl.gen_latent_rope(B * ctx, seed + 10 * r, device)
+            slots = torch.cat([wl.slot_mapping_for(bt, b, 0, ctx) for b in range(B)])
+            m.mla_nvfp4_quantize_append(lat, rope, slots, cache, PAGE)
+            del lat, rope
+            self.caches.append(cache)
+            self.tables.append(bt)
+        self.rot = rotations
+        self.q = [wl.gen_queries(B, 1, H, "bf16", seed + 100 + r, device) for r in range(rotations)]
+        self.seq = torch.full((B,), ctx, dtype=torch.int32, device=device)
+        self.splits = m.mla_dense_decode_num_splits(self.tables[0].shape[1], split_tokens)
+        self.ws = torch.empty(max(m.mla_decode_workspace_size(B, H, self.splits), 256),
+                              dtype=torch.uint8, device=device)
+        self.out = torch.empty(B, 1, H, 512, dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, 1, H, dtype=torch.float32, device=device)
+        torch.cuda.synchronize()
+
+    def decode(self, r):
+        import nvfp4_compressed_mla_amd as m
+        m.mla_dense_decode(self.q[r], self.caches[r], PAGE, self.tables[r], self.seq,
+                           1.0 / math.sqrt(576.0), split_tokens=self.split_tokens, out=self.out,
+                           lse=self.lse, workspace=self.ws)
+
+    step = decode
+
+    def kernel_bytes(self, r):
+        return self.B * self.ctx * (352 + 4 / 64) + self.B * self.H * 576 * 2
+
+    def gathered_bytes(self, r):
+        return self.B * self.ctx * 352
+
+    def flops(self, r):
+        return self.B * self.ctx * 2 * self.H * (576 + 512)
+
+
+# ---- timing helpers ----------------------------------------------------------------------------
+
+def capture(fn, n, offset=0):
+    """Capture fn(offset), ..., fn(offset+n-1) into one HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            fn(offset + i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(offset + i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(fn, rot, steps, warmup):
+    """Replay captured graphs for `warmup` then exactly `steps` steps; returns wall ms per step."""
+    import torch
+    full = capture(fn, rot)
+    singles = {}
+
+    def run(n):
+        for _ in range(n // rot):
+            full.replay()
+        for r in range(n % rot):
+            if r not in singles:
+                singles[r] = capture(fn, 1, r)
+            singles[r].replay()
+
+    # capture any single-step graphs the timed region needs before timing
+    for r in range(steps % rot):
+        singles[r] = capture(fn, 1, r)
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps
+
+
+def time_decode_kernel(wk, launches):
+    """Average fused-decode-kernel duration (ms) from library-recorded HIP events, eager launches."""
+    import torch
+    import nvfp4_compressed_mla_amd as m
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(launches)]
+    for a, b in pairs:                      # materialise the underlying HIP events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    try:
+        for i, (a, b) in enumerate(pairs):
+            m.mla_set_timing_events(a.cuda_event, b.cuda_event)
+            wk.decode(i % wk.rot)
+    finally:
+        m.mla_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in pairs]
+    durs = durs[min(5, len(durs) // 4):]    # first launches of a cold process excluded
+    return sum(durs) / len(durs), durs
+
+
+def counters_traffic(src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; None otherwise."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---- CPU oracle baseline -----------------------------------------------------------------------
+
+def cpu_baseline(wk, budget_s=12.0):
+    """The CPU oracle (fp64 NumPy, untuned) on the same step: quantize the step's new rows and
+    decode all query tokens of rotation 0 from a cache the oracle built itself from the same bf16
+    rows. Setup (oracle quantization of the selected rows) is untimed. Repeats whole steps until
+    ``budget_s`` elapsed."""
+    import numpy as np
+    import torch
+    from oracle import attention as oa
+    from oracle import cache as oc
+    from oracle import nvfp4 as nv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    idx = wk.idx[0].cpu().numpy()
+    bt = wk.block_table.cpu().numpy()
+    q = wk.q[0].float().cpu().numpy().astype(np.float64)
+    cache = np.zeros(wk.cache.numel(), dtype=np.uint8)
+    for b in range(wk.B):
+        pos = np.unique(idx[b][idx[b] >= 0])
+        rows = torch.as_tensor(wk.row_base[b] + pos, device=wk.latent.device)
+        enc = nv.quantize_rows(wk.latent[rows].double().cpu().numpy(), wk.rope[rows].double().cpu().numpy())
+        oc.write_rows(cache, PAGE, [oc.logical_slot(bt[b], int(j)) for j in pos], enc)
+    new_lat = wk.new_lat.double().cpu().numpy()
+    new_rope = wk.new_rope.double().cpu().numpy()
+    new_slots = wk.new_slots.cpu().numpy()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oc.write_rows(cache, PAGE, new_slots, nv.quantize_rows(new_lat, new_rope))
+        oa.sparse_decode(q, cache, PAGE, bt, idx, 1.0 / math.sqrt(576.0))
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {
+        "value": round(wk.gathered_bytes(0) / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n} whole step(s) of the batched config ({wk.B * wk.q_len} query tokens x "
+                   f"{wk.topk} rows + {wk.append_rows * wk.B} appended rows), "
+                   f"{dt * 1e3:.0f} ms per step; host cpus visible: {len(os.sched_getaffinity(0))}"),
+    }
+
+
+# ---- main --------------------------------------------------------------------------------------
+
+def run_config(wk, steps, warmup, prof_launches):
+    """Graph-timed decode launches plus event-timed fused kernel for one extra config."""
+    ms = time_steps(wk.decode, wk.rot, steps, warmup)
+    kavg, _ = time_decode_kernel(wk, prof_launches)
+    nb = sum(wk.kernel_bytes(r) for r in range(wk.rot)) / wk.rot
+    gb = sum(wk.gathered_bytes(r) for r in range(wk.rot)) / wk.rot
+    fl = sum(wk.flops(r) for r in range(wk.rot)) / wk.rot
+    return {
+        "us_per_launch": round(ms * 1e3, 2),
+        "fused_kernel_us": round(kavg * 1e3, 2),
+        "gathered_GBps": round(gb / (ms * 1e-3) / 1e9, 1),
+        "kernel_GBps": round(nb / (kavg * 1e-3) / 1e9, 1),
+        "kernel_hbm_frac": round(nb / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kernel_TFLOPs": round(fl / (kavg * 1e-3) / 1e12, 1),
+        "kernel_mfma_frac": round(fl / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+        "splits": wk.splits,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--warmup", type=int, default=96)
+    ap.add_argument("--rotations", type=int, default=48)
+    ap.add_argument("--prof-launches", type=int, default=64)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "copies": 3}))
+        return
+
+    import nvfp4_compressed_mla_amd as m
+    m.load_library()                         # raises if the HIP library was not built
+
+    log("[bench] building batched workload (B=32, H=64, 143,360-token caches, top-k 2048)")
+    t_setup = time.perf_counter()
+    wk = SparseWorkload("batched", B=32, q_len=1, H=64, ctx=[143360 + 1] * 32, topk=2048,
+                        append_rows=1, rotations=args.rotations, seed=1001, device=dev,
+                        keep_latent=not args.no_cpu_baseline)
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; splits={wk.splits}")
+
+    ms_step = time_steps(wk.step, wk.rot, args.steps, args.warmup)
+    log(f"[bench] step {ms_step * 1e3:.2f} us")
+    ms_dec = time_steps(wk.decode, wk.rot, max(args.steps // 2, wk.rot), args.warmup)
+    kavg, kd = time_decode_kernel(wk, args.prof_launches)
+    log(f"[bench] decode launch {ms_dec * 1e3:.2f} us, fused kernel {kavg * 1e3:.2f} us")
+
+    gathered = sum(wk.gathered_bytes(r) for r in range(wk.rot)) / wk.rot
+    kbytes = sum(wk.kernel_bytes(r) for r in range(wk.rot)) / wk.rot
+    flops = sum(wk.flops(r) for r in range(wk.rot)) / wk.rot
+    achieved = kbytes / (kavg * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = counters_traffic(src_hash)
+
+    result = {
+        "metric": "sparse-MLA decode us/launch + achieved HBM GB/s (% of peak), 140K ctx top-k 2048",
+        "value": round(gathered / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "batched sparse decode step: B=32, q_len=1, H=64, ctx 143,360 "
+                               "(+1 appended row per request), top-k 2048, 64-row pages, random "
+                               "block tables",
+                   "global_batch": 32, "seq_len": 143360, "topk": 2048, "heads": 64,
+                   "rotations": wk.rot, "splits": wk.splits},
+        "us_per_launch": round(ms_dec * 1e3, 2),
+        "gathered_GBps_per_launch": round(gathered / (ms_dec * 1e-3) / 1e9, 1),
+        "gathered_pct_of_peak": round(100 * gathered / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<4,false> (fused gather/decode/QK/softmax/PV)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel_us": round(kavg * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(kbytes),
+            "mfma_TFLOPs": round(flops / (kavg * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+            "kernel_source_sha256_16": src_hash,
+        },
+        "context": {"pages_GB200_us_per_launch_15tok_16heads": 12.0},
+    }
+
+    if not args.no_extra:
+        extra = {}
+        for name, mk in (
+            ("pages_shape_T15_H16", lambda: SparseWorkload("pages", 1, 15, 16, [149504], 2048, 0, 64, 1101, dev)),
+            ("mtp_B16_q15_H64", lambda: SparseWorkload("mtp", 16, 15, 64, [149504] * 16, 2048, 0, 6, 1002, dev)),
+            ("tiny_B1_H16_k256", lambda: SparseWorkload("tiny", 1, 1, 16, [4096], 256, 0, 8, 1000, dev)),
+        ):
+            log(f"[bench] extra: {name}")
+            w2 = mk()
+            extra[name] = run_config(w2, 192, 24, 32)
+            del w2
+            torch.cuda.empty_cache()
+        log("[bench] extra: dense_B8_H64_146K")
+        dw = DenseWorkload(8, 64, 149504, 4096, 3, 1003, dev)
+        extra["dense_B8_H64_146K_split4096"] = run_config(dw, 48, 6, 24)
+        del dw
+        torch.cuda.empty_cache()
+        log("[bench] extra: mixed serving step")
+        from nvfp4_compressed_mla_amd import workloads as wl
+        mx = wl.named_workload("mixed")
+        # history lengths log-uniform in [4K, 200K]; the step appends 6144 rows to each request
+        mw = SparseWorkload("mixed", mx.B, 15, 64, [c + 6144 for c in mx.ctx], 2048, 6144, 4, 1004,
+                            dev, q_lens=mx.q_lens)
+        ms_mixed = time_steps(mw.step, mw.rot, 16, 4)
+        t0 = time.perf_counter()
+        for _ in range(8):
+            mw.append()
+        torch.cuda.synchronize()
+        ms_app = (time.perf_counter() - t0) * 1e3 / 8
+        extra["mixed_B64_step"] = {
+            "ms_per_step": round(ms_mixed, 4),
+            "append_rows": 6144 * 64,
+            "append_ms_eager": round(ms_app, 4),
+            "append_GBps_eager": round(6144 * 64 * (1152 + 352 + 8) / (ms_app * 1e-3) / 1e9, 1),
+            "decode": run_config(mw, 16, 4, 12),
+        }
+        del mw
+        torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wk, args.cpu_seconds)
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

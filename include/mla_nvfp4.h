@@ -86,8 +86,8 @@ mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stri
 size_t mla_decode_workspace_size(int32_t num_tokens, int32_t H, int32_t num_splits);
 
 /* Number of row splits mla_sparse_decode will use for this shape when `max_splits` = 0 (auto,
- * sized so that the launch covers one wave of the 256 compute units), or min(max_splits, topk/32)
- * otherwise. The caller sizes the workspace with this number. */
+ * sized so that the launch covers one wave of the 256 compute units), or min(max_splits, topk/64)
+ * otherwise (each split keeps at least 64 list entries). The caller sizes the workspace with this number. */
 int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk,
                                      int32_t max_splits);
 
@@ -119,7 +119,7 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype,
 
 /* Dense decode over the whole cache of each request (no indexer): query token t of request b
  * attends to logical positions 0 .. seq_lens[b]-q_len+t (causal inside the step), split into
- * chunks of split_tokens positions (a multiple of 32) merged by log-sum-exp.
+ * chunks of split_tokens positions (a multiple of 64, at most 8192) merged by log-sum-exp.
  *   seq_lens   int32 [B] device array; values above max_pages*64 are clamped.
  *   Other arguments as mla_sparse_decode; num_splits from mla_dense_decode_num_splits. */
 mla_status mla_dense_decode(const void* q, mla_dtype q_dtype,
@@ -135,6 +135,13 @@ mla_status mla_dense_decode(const void* q, mla_dtype q_dtype,
 mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,
                                      int64_t cache_bytes, const int64_t* slots, int64_t n,
                                      float* out, hipStream_t stream);
+
+/* Profiling hook, off the hot path: when `start`/`stop` are non-null, every later
+ * mla_sparse_decode / mla_dense_decode call on this host thread records `start` on its stream
+ * right before the fused decode kernel(s) and `stop` right after them (before the split-combine
+ * kernel), so hipEventElapsedTime gives the fused kernel's own duration. Pass nulls to turn it
+ * off. The events are owned by the caller; they must not be recorded inside a graph capture. */
+mla_status mla_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);

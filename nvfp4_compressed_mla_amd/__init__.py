@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     mla_dense_decode_num_splits,
     mla_nvfp4_dequantize_rows,
     mla_nvfp4_quantize_append,
+    mla_set_timing_events,
     mla_sparse_decode,
     mla_sparse_decode_num_splits,
 )

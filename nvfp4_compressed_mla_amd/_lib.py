@@ -28,6 +28,7 @@ EXPORTED = [
     "mla_sparse_decode",
     "mla_dense_decode",
     "mla_nvfp4_dequantize_rows",
+    "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
 ]
@@ -50,6 +51,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m nvfp4_compressed_mla_amd.build`")
+    try:
+        # torch first: its HIP runtime then also serves this library (one runtime per process,
+        # so torch streams and events are valid handles here)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.mla_nvfp4_quantize_append.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp]
@@ -68,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_dense_decode.restype = ctypes.c_int
     lib.mla_nvfp4_dequantize_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.mla_nvfp4_dequantize_rows.restype = ctypes.c_int
+    lib.mla_set_timing_events.argtypes = [vp, vp]
+    lib.mla_set_timing_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -254,3 +263,8 @@ def mla_nvfp4_dequantize_rows(kv_cache, page_stride_bytes, slots, stream=None):
     _check(lib.mla_nvfp4_dequantize_rows(_ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
                                          _ptr(slots), slots.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+def mla_set_timing_events(start, stop) -> None:
+    """Record raw HIP events (handles as ints / c_void_p, or None) around the fused decode kernel."""
+    _check(load_library().mla_set_timing_events(start, stop))

@@ -21,6 +21,9 @@ FLAGS = [
     # packed FP32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # keep MFMA accumulators in VGPRs: the softmax rescale multiplies them with VALU, and an
+    # AGPR home for them costs a full AGPR<->VGPR copy of the output tile on every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -12,6 +12,8 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_timing_start = nullptr;
+thread_local hipEvent_t g_timing_stop = nullptr;
 
 mla_status fail(mla_status s, const char* fmt, ...) {
   va_list ap;
@@ -45,9 +47,8 @@ mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_
   return MLA_OK;
 }
 
-// One group of up to 64 heads per workgroup; the number of workgroups a single wave of the chip
-// holds depends on how many heads a group carries (register footprint).
-int waves_capacity(int32_t H) { return H >= 64 ? kComputeUnits : 2 * kComputeUnits; }
+// Workgroups one wave of the chip holds: two per compute unit.
+int waves_capacity(int32_t) { return 2 * kComputeUnits; }
 
 size_t ws_bytes(int64_t T, int64_t H, int64_t S) {
   if (S <= 1) return 0;
@@ -73,7 +74,7 @@ mla_status check_decode_common(const void* q, mla_dtype q_dtype, const void* kv_
   if (lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (num_splits < 1 || num_splits > 4096) return fail(MLA_ERR_INVALID_ARG, "num_splits %d out of range", num_splits);
   const int64_t T = (int64_t)B * q_len;
-  if (T * num_splits * ((H + 63) / 64) > (int64_t)1 << 28) return fail(MLA_ERR_INVALID_ARG, "launch too large");
+  if (T * num_splits * (H / 16) > (int64_t)1 << 28) return fail(MLA_ERR_INVALID_ARG, "launch too large");
   if (num_splits > 1) {
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
     if (!aligned(workspace, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -84,29 +85,30 @@ mla_status check_decode_common(const void* q, mla_dtype q_dtype, const void* kv_
   return MLA_OK;
 }
 
+// Heads per workgroup: 32 when H allows it, else 16 (H is a multiple of 16).
+int32_t head_group(int32_t H) { return (H % 32 == 0) ? 32 : 16; }
+
 mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, hipStream_t stream) {
   const int64_t T = (int64_t)a.B * a.q_len;
-  const int32_t full = H / 64, tail = (H % 64) / 16;
+  const int32_t G = head_group(H);
   const int32_t S = a.n_split;
   const int32_t T32 = (int32_t)T;
-  if (full > 0) {
-    a.hg_begin = 0;
-    a.n_hg = full;
-    a.total_items = T32 * full * S;
-    a.items_per_xcd = (a.total_items + 7) / 8;
-    hipError_t e = mla::launch_decode(a, 4, dense, stream);
-    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+  if (g_timing_start) {
+    hipError_t e = hipEventRecord(g_timing_start, stream);
+    if (e != hipSuccess) return hip_status(e, "timing start event");
   }
-  if (tail > 0) {
-    a.hg_begin = full;
-    a.n_hg = 1;
-    a.total_items = T32 * S;
-    a.items_per_xcd = (a.total_items + 7) / 8;
-    hipError_t e = mla::launch_decode(a, tail, dense, stream);
-    if (e != hipSuccess) return hip_status(e, "decode kernel launch (tail head group)");
+  a.hg_begin = 0;
+  a.n_hg = H / G;
+  a.total_items = T32 * a.n_hg * S;
+  a.items_per_xcd = (a.total_items + 7) / 8;
+  hipError_t e = mla::launch_decode(a, G / 16, dense, stream);
+  if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+  if (g_timing_stop) {
+    e = hipEventRecord(g_timing_stop, stream);
+    if (e != hipSuccess) return hip_status(e, "timing stop event");
   }
   if (S > 1) {
-    hipError_t e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
+    e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
     if (e != hipSuccess) return hip_status(e, "combine kernel launch");
   }
   return hip_status(hipSuccess, "");
@@ -128,6 +130,14 @@ const char* mla_status_string(mla_status s) {
 }
 
 const char* mla_last_error(void) { return g_last_error; }
+
+mla_status mla_set_timing_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "timing events must be both set or both null");
+  g_timing_start = start;
+  g_timing_stop = stop;
+  return MLA_OK;
+}
 
 mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride,
                                      const void* rope, int64_t rope_row_stride,
@@ -159,7 +169,7 @@ int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk
   if (num_tokens < 1 || H < 16 || topk < 1) return 1;
   const int32_t cap_by_rows = topk >= 64 ? topk / 64 : 1;    // keep >= 64 rows per split
   if (max_splits > 0) return max_splits < cap_by_rows ? max_splits : cap_by_rows;
-  const int64_t groups = (H + 63) / 64;
+  const int64_t groups = H / ((H % 32 == 0) ? 32 : 16);
   const int64_t items = (int64_t)num_tokens * groups;
   const int64_t cap = waves_capacity(H);
   // Smallest split count whose items fill ~90% of one wave of workgroups.

@@ -8,7 +8,9 @@
 // results are merged; -1 entries of the index list are skipped instead of being loaded.
 //
 // MI355X design (not the page's Blackwell design):
-//  * One workgroup = 4 wavefronts = one (query token, head group of up to 64 heads, row split).
+//  * One workgroup = 4 wavefronts = one (query token, head group of 16 or 32 heads, row split);
+//    two workgroups share a compute unit (<= 256 registers per lane, <= 80 KB LDS each), so the
+//    hardware interleaves one group's MFMA work with the other's decode and softmax.
 //    The 576 QK dimensions and the 512 output dimensions are partitioned across the 4 waves:
 //    wave w owns latent dims [128w, 128w+128) and rope dims [16w, 16w+16). Every row is therefore
 //    decoded exactly once per workgroup, and each wave keeps only its slice of the queries
@@ -85,16 +87,32 @@ __device__ __forceinline__ half8v q_to_half8(const void* q, int64_t off, bool fp
   return h;
 }
 
+// Max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48), with the gfx950
+// lane-swap instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float4v mfma16(half8v a, half8v b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 template <int NH, bool DENSE>
-__global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, (NH <= 2) ? 2 : 1) void decode_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kNBuf][kStageBytes];
   __shared__ __attribute__((aligned(16))) float4v sred[4][NH][2][64];
   __shared__ __attribute__((aligned(16))) half8v pbuf[NH][64];
   __shared__ __attribute__((aligned(16))) float alpha_s[64];
+  __shared__ int32_t rescale_s[4];
   __shared__ __attribute__((aligned(16))) float mfin[64];
   __shared__ __attribute__((aligned(16))) float lfin[64];
   __shared__ uint32_t rowoff[DENSE ? kMaxDensePages : kMaxSplitRows];
@@ -110,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const int hg = a.hg_begin + rest % a.n_hg;
   const int tok = rest / a.n_hg;
   const int b = tok / a.q_len, t = tok % a.q_len;
-  const int head0 = hg * 64;
+  const int head0 = hg * 16 * NH;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
   // ---- rows of this split -------------------------------------------------------------------
@@ -181,32 +199,43 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     const half8v r = q_to_half8(a.q, qrow + kLatent + 16 * w + 8 * (kg & 1), a.q_fp32);
     qa[hb][4] = (kg < 2) ? r : half8v{};
   }
+  // Make the query fragments opaque so the compiler keeps them in registers instead of
+  // re-loading and re-converting them from memory inside the tile loop.
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+    for (int c = 0; c < 5; ++c) asm volatile("" : "+v"(qa[hb][c]));
 
   // ---- tile loader --------------------------------------------------------------------------
+  // Each lane moves 16-byte pieces p = (j*4 + w)*64 + lane of the tile (22 pieces per row): the
+  // row offsets are read from LDS together, then every lane issues its loads, with padding
+  // pieces and rows past the end reading the zero row (no divergent branches).
   auto issue_tile = [&](int tile) {
     uint8_t* dst = stage[tile % kNBuf];
+    uint32_t o16[kLoadsPerWave];
+    int ri[kLoadsPerWave], piece[kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int p = min((j * 4 + w) * 64 + lane, kPiecesPerTile - 1);
+      const int r = p / 22;
+      piece[j] = p - r * 22;
+      ri[j] = tile * kTileRows + r;
+      const int rc = min(ri[j], n_rows - 1);
+      if constexpr (!DENSE) {
+        o16[j] = rowoff[rc];
+      } else {
+        const int pos = p0 + rc;
+        const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
+        o16[j] = (pb == kInvalid) ? kInvalid : pb + (uint32_t)(pos & 63) * (kRowBytes / 16);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j) {
       const int p = (j * 4 + w) * 64 + lane;
-      const uint8_t* src = g_zero_row;
-      if (p < kPiecesPerTile) {
-        const int r = p / 22;
-        const int piece = p - r * 22;
-        const int ri = tile * kTileRows + r;
-        src = g_zero_row + piece * 16;
-        if (ri < n_rows) {
-          uint32_t o16;
-          if constexpr (!DENSE) {
-            o16 = rowoff[ri];
-          } else {
-            const int pos = p0 + ri;
-            const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-            o16 = (pb == kInvalid) ? kInvalid : pb + (uint32_t)(pos & 63) * (kRowBytes / 16);
-            if (o16 != kInvalid && (int64_t)o16 * 16 + kRowBytes > a.cache_bytes) o16 = kInvalid;
-          }
-          if (o16 != kInvalid) src = a.cache + (int64_t)o16 * 16 + piece * 16;
-        }
-      }
+      bool ok = p < kPiecesPerTile && ri[j] < n_rows && o16[j] != kInvalid;
+      if constexpr (DENSE) ok = ok && (int64_t)o16[j] * 16 + kRowBytes <= a.cache_bytes;
+      const uint8_t* src = ok ? a.cache + (int64_t)o16[j] * 16 + piece[j] * 16
+                              : g_zero_row + piece[j] * 16;
       __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(dst + (j * 4 + w) * 1024), 16, 0, 0);
     }
   };
@@ -218,6 +247,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[hb][c] = float4v{0.f, 0.f, 0.f, 0.f};
 
+  if (w >= NH && lane == 0) rescale_s[w] = 0;       // these waves own no head block
   const int n_tiles = (n_rows + kTileRows - 1) / kTileRows;
   if (n_tiles > 0) issue_tile(0);
   if (n_tiles > 1) issue_tile(1);
@@ -229,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     const uint8_t* tb = stage[i % kNBuf];
 
     // -- QK: partial S^T over this wave's 144 dims, all heads -----------------------------------
-    float4v acc[NH][2];
+    half8v kf[2][5];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint8_t* row = tb + (16 * h + l16) * kRowBytes;
@@ -237,34 +267,35 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       const uint32_t sc = *(const uint16_t*)(row + kScaleOff + 8 * w + 2 * kg);
       const uint2v rp = *(const uint2v*)(row + kRopeOff + 16 * w + 8 * (kg & 1));
       const half2v s0 = scale_pair(sc & 0xFFu), s1 = scale_pair(sc >> 8);
-      half8v kf[5];
-      kf[0] = decode_fp4x8(cw[0], s0);
-      kf[1] = decode_fp4x8(cw[1], s0);
-      kf[2] = decode_fp4x8(cw[2], s1);
-      kf[3] = decode_fp4x8(cw[3], s1);
-      kf[4] = (kg < 2) ? decode_fp8x8(rp[0], rp[1]) : half8v{};
-#pragma unroll
-      for (int hb = 0; hb < NH; ++hb) {
-        float4v c4 = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 5; ++c) c4 = mfma16(kf[c], qa[hb][c], c4);
-        acc[hb][h] = c4;
-      }
+      kf[h][0] = decode_fp4x8(cw[0], s0);
+      kf[h][1] = decode_fp4x8(cw[1], s0);
+      kf[h][2] = decode_fp4x8(cw[2], s1);
+      kf[h][3] = decode_fp4x8(cw[3], s1);
+      kf[h][4] = (kg < 2) ? decode_fp8x8(rp[0], rp[1]) : half8v{};
     }
+    // chunk-major: consecutive MFMAs feed different accumulators (a dependent MFMA would wait
+    // for its predecessor to drain)
+    float4v acc[NH][2];
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb)
-      if (hb != w) { sred[w][hb][0][lane] = acc[hb][0]; sred[w][hb][1][lane] = acc[hb][1]; }
+    for (int hb = 0; hb < NH; ++hb) { acc[hb][0] = float4v{0.f, 0.f, 0.f, 0.f}; acc[hb][1] = acc[hb][0]; }
+#pragma unroll
+    for (int c = 0; c < 5; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb) acc[hb][h] = mfma16(kf[h][c], qa[hb][c], acc[hb][h]);
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {       // every block, the owner's too: no branch
+      sred[w][hb][0][lane] = acc[hb][0];
+      sred[w][hb][1][lane] = acc[hb][1];
+    }
     lds_barrier();
 
     // -- online softmax on the owning wave ------------------------------------------------------
     if (w < NH) {
-      float4v s0 = float4v{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      float4v s0 = sred[0][w][0][lane], s1 = sred[0][w][1][lane];
 #pragma unroll
-      for (int hb = 0; hb < NH; ++hb)
-        if (hb == w) { s0 = acc[hb][0]; s1 = acc[hb][1]; }
-#pragma unroll
-      for (int src = 0; src < 4; ++src)
-        if (src != w) { s0 += sred[src][w][0][lane]; s1 += sred[src][w][1][lane]; }
+      for (int src = 1; src < 4; ++src) { s0 += sred[src][w][0][lane]; s1 += sred[src][w][1][lane]; }
       float sv[8];
       float mx = -INFINITY;
 #pragma unroll
@@ -274,27 +305,36 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
         sv[4 + r] = (rb < n_rows) ? s1[r] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, fmaxf(sv[r], sv[4 + r]));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      mx = group4_max(mx);
+      // The running max moves lazily: only when a tile's max exceeds it by more than 2^8, so the
+      // probabilities stay <= 256 (exact range for FP16) and O is rescaled only on those tiles.
+      const bool move = mx > m_run + 8.0f;        // also true on the first tile (m_run = -inf)
+      const float m_new = move ? mx : m_run;
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       half8v pf;
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const _Float16 p = none ? (_Float16)0.0f : (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
         pf[e] = p;
         psum += (float)p;
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
+      const uint64_t any = __ballot(move && i > 0);
+      if (lane == 0) rescale_s[w] = any != 0ull;
       pbuf[w][lane] = pf;
       if (kg == 0) alpha_s[16 * w + l16] = alpha;
     }
     lds_barrier();
 
-    // -- PV: this wave's 128 output dims, all heads ---------------------------------------------
+    // -- PV: this wave's 128 output dims, all heads ----------------------------------------------
+    half8v pfr[NH];
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) pfr[hb] = pbuf[hb][lane];
+    const bool rescale = (rescale_s[0] | rescale_s[1] | rescale_s[2] | rescale_s[3]) != 0;
+    // V fragments: 8 tokens of one dim per lane (the P fragment's token slots), decoded while the
+    // P fragments are in flight.
     uint32_t D[8], SB[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -320,20 +360,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       x = fp4x2_to_half2<3>(ze) * sab; v[6][2 * pr] = x[0]; v[6][2 * pr + 1] = x[1];
       x = fp4x2_to_half2<3>(zo) * sab; v[7][2 * pr] = x[0]; v[7][2 * pr + 1] = x[1];
     }
+    if (rescale) {
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      const float4v al = *(const float4v*)&alpha_s[16 * hb + 4 * kg];
-      const half8v pfr = pbuf[hb][lane];
+      for (int hb = 0; hb < NH; ++hb) {
+        const float4v al = *(const float4v*)&alpha_s[16 * hb + 4 * kg];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[hb][c] = mfma16(pfr, v[c], o[hb][c] * al);
+        for (int c = 0; c < 8; ++c) o[hb][c] *= al;
+      }
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb) o[hb][c] = mfma16(pfr[hb], v[c], o[hb][c]);
   }
 
   // ---- normalise and write ------------------------------------------------------------------
   if (w < NH) {
-    float lt = l_run;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = group4_sum(l_run);
     if (kg == 0) { mfin[16 * w + l16] = m_run; lfin[16 * w + l16] = lt; }
   }
   lds_barrier();
