@@ -41,6 +41,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def head_group_blocks(H: int) -> int:
+    """16-head blocks per decode workgroup (the library's head grouping: 32 heads when H % 32 == 0)."""
+    return 2 if H % 32 == 0 else 1
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -416,7 +421,7 @@ def main():
         "gathered_pct_of_peak": round(100 * gathered / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<4,false> (fused gather/decode/QK/softmax/PV)",
+            "kernel": f"decode_kernel<{head_group_blocks(64)},false> (fused gather/decode/QK/softmax/PV)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -46,8 +46,13 @@ def softmax_scale() -> float:
 
 
 def build_case(B, q_len, H, ctx, topk, seed, q_dtype="bf16", page_stride=PAGE_BYTES,
-               device="cuda", spare_pages=3, topk_fn=None):
-    """Generate inputs on the device and quantize them into a paged cache with the HIP path."""
+               device="cuda", spare_pages=3, topk_fn=None, append_rows=0):
+    """Generate inputs on the device and quantize them into a paged cache with the HIP path.
+
+    ``append_rows`` > 0 writes the last ``append_rows`` positions of every request with a second
+    quantize-append call covering all requests at once (a serving step's append), after the
+    history rows.
+    """
     from nvfp4_compressed_mla_amd import mla_nvfp4_quantize_append
     ctx = list(ctx)
     total = sum(ctx)
@@ -57,8 +62,21 @@ def build_case(B, q_len, H, ctx, topk, seed, q_dtype="bf16", page_stride=PAGE_BY
     row_base = [0]
     for c in ctx[:-1]:
         row_base.append(row_base[-1] + c)
-    slots = torch.cat([wl.slot_mapping_for(bt, b, 0, c) for b, c in enumerate(ctx)])
-    mla_nvfp4_quantize_append(latent, rope, slots, cache, page_stride)
+    hist = [c - append_rows for c in ctx]
+    if min(hist) < 0:
+        raise ValueError("append_rows exceeds a context length")
+    slots = torch.cat([wl.slot_mapping_for(bt, b, 0, c) for b, c in enumerate(hist)])
+    if append_rows:
+        rows = torch.cat([torch.arange(row_base[b], row_base[b] + c, device=device)
+                          for b, c in enumerate(hist)])
+        mla_nvfp4_quantize_append(latent[rows], rope[rows], slots, cache, page_stride)
+    else:
+        mla_nvfp4_quantize_append(latent, rope, slots, cache, page_stride)
+    if append_rows:
+        slots = torch.cat([wl.slot_mapping_for(bt, b, hist[b], append_rows) for b in range(B)])
+        rows = torch.cat([torch.arange(row_base[b] + hist[b], row_base[b] + ctx[b], device=device)
+                          for b in range(B)])
+        mla_nvfp4_quantize_append(latent[rows], rope[rows], slots, cache, page_stride)
     q = wl.gen_queries(B, q_len, H, q_dtype, seed + 2, device)
     idx = None
     if topk:
