@@ -47,8 +47,8 @@ mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_
   return MLA_OK;
 }
 
-// Workgroups one wave of the chip holds: two per compute unit.
-int waves_capacity(int32_t) { return 2 * kComputeUnits; }
+// Decode workgroups resident at once: one per compute unit (512 threads, ~120 KB of LDS).
+int waves_capacity(int32_t) { return kComputeUnits; }
 
 size_t ws_bytes(int64_t T, int64_t H, int64_t S) {
   if (S <= 1) return 0;
@@ -85,30 +85,40 @@ mla_status check_decode_common(const void* q, mla_dtype q_dtype, const void* kv_
   return MLA_OK;
 }
 
-// Heads per workgroup: 32 when H allows it, else 16 (H is a multiple of 16).
-int32_t head_group(int32_t H) { return (H % 32 == 0) ? 32 : 16; }
+// Workgroups per token (all launches together) for H heads.
+int32_t head_groups(int32_t H) {
+  const int32_t nb = H / 16;
+  return nb / 4 + (nb % 4 != 0 ? 1 : 0);
+}
 
 mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, hipStream_t stream) {
   const int64_t T = (int64_t)a.B * a.q_len;
-  const int32_t G = head_group(H);
   const int32_t S = a.n_split;
   const int32_t T32 = (int32_t)T;
   if (g_timing_start) {
     hipError_t e = hipEventRecord(g_timing_start, stream);
     if (e != hipSuccess) return hip_status(e, "timing start event");
   }
-  a.hg_begin = 0;
-  a.n_hg = H / G;
-  a.total_items = T32 * a.n_hg * S;
-  a.items_per_xcd = (a.total_items + 7) / 8;
-  hipError_t e = mla::launch_decode(a, G / 16, dense, stream);
-  if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+  const int32_t nb = H / 16;
+  const int32_t full = nb / 4, tail = nb % 4;
+  // launch 1: groups of 64 heads; launch 2: the remaining 16..48 heads
+  for (int part = 0; part < 2; ++part) {
+    const int32_t nh = part == 0 ? 4 : tail;
+    const int32_t groups = part == 0 ? full : (tail ? 1 : 0);
+    if (groups == 0) continue;
+    a.head_begin = part == 0 ? 0 : full * 64;
+    a.n_hg = groups;
+    a.total_items = T32 * groups * S;
+    a.items_per_xcd = (a.total_items + 7) / 8;
+    hipError_t e = mla::launch_decode(a, nh, dense, stream);
+    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+  }
   if (g_timing_stop) {
-    e = hipEventRecord(g_timing_stop, stream);
+    hipError_t e = hipEventRecord(g_timing_stop, stream);
     if (e != hipSuccess) return hip_status(e, "timing stop event");
   }
   if (S > 1) {
-    e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
+    hipError_t e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
     if (e != hipSuccess) return hip_status(e, "combine kernel launch");
   }
   return hip_status(hipSuccess, "");
@@ -169,7 +179,7 @@ int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk
   if (num_tokens < 1 || H < 16 || topk < 1) return 1;
   const int32_t cap_by_rows = topk >= 64 ? topk / 64 : 1;    // keep >= 64 rows per split
   if (max_splits > 0) return max_splits < cap_by_rows ? max_splits : cap_by_rows;
-  const int64_t groups = H / ((H % 32 == 0) ? 32 : 16);
+  const int64_t groups = head_groups(H);
   const int64_t items = (int64_t)num_tokens * groups;
   const int64_t cap = waves_capacity(H);
   // Smallest split count whose items fill ~90% of one wave of workgroups.

@@ -7,35 +7,33 @@
 // FP32 accumulation; a query token's rows are split across cooperating blocks whose partial
 // results are merged; -1 entries of the index list are skipped instead of being loaded.
 //
-// MI355X design (not the page's Blackwell design):
-//  * One workgroup = 4 wavefronts = one (query token, head group of 16 or 32 heads, row split);
-//    two workgroups share a compute unit (<= 256 registers per lane, <= 80 KB LDS each), so the
-//    hardware interleaves one group's MFMA work with the other's decode and softmax.
-//    The 576 QK dimensions and the 512 output dimensions are partitioned across the 4 waves:
-//    wave w owns latent dims [128w, 128w+128) and rope dims [16w, 16w+16). Every row is therefore
-//    decoded exactly once per workgroup, and each wave keeps only its slice of the queries
-//    (FP16, 5 MFMA k-chunks x NH head blocks) and of the output accumulators in registers.
-//  * Rows are gathered 32 at a time into a 3-slot LDS ring with gfx950 direct-to-LDS 16-byte
-//    loads (global_load_lds_dwordx4), two tiles ahead of the math (the page's three-slot buffer,
-//    as an LDS ring). Empty and out-of-range slots never reach the ring: sparse index lists are
-//    compacted up front, and padding rows read a zero row.
-//  * QK: v_mfma_f32_16x16x32_f16 with the decoded rows as the A operand (lane = token, 8 dims =
-//    one packed dword + its group scale) and the query slice as B, giving S^T blocks whose lanes
-//    hold 4 tokens of one head. The four per-wave partial score blocks are summed through LDS
-//    (reduce-scatter: wave h owns head block h).
-//  * Online softmax in FP32 (base-2, log2(e) folded into the scale) on the owning wave; the
-//    probabilities are rounded to FP16 and, thanks to the S^T layout, each lane already holds the
-//    8 token-slots of one head that form an MFMA A fragment, so P goes to LDS as 16-byte
-//    fragments with no transpose.
-//  * PV: each wave multiplies P by its 128-dim slice of the latent. The B operand needs 8 tokens
-//    of one dim per lane: a lane reads one code dword (8 dims) from each of 8 rows, interleaves
-//    the nibbles of token pairs, converts with v_cvt_scalef32_pk_f16_fp4 and applies the two
-//    tokens' scales with one packed FP16 multiply; the 8 nibble positions feed 8 MFMAs whose
-//    output columns are dims 8n+c.
-//  * Splits write normalised partial outputs and their log-sum-exp; combine_kernel merges them
-//    in split order (deterministic). With a single split the kernel writes the final output.
-//  * Workgroup i is placed on XCD i % 8 by the hardware; items are remapped so that the splits
-//    of one token are consecutive on one XCD and share its L2.
+// MI355X design (not the page's Blackwell design). On gfx950 an MFMA and a VALU instruction of
+// the same wave do not overlap, while those of two waves sharing a SIMD do. The workgroup is
+// therefore split by role (per SIMD one math wave and two producer waves), and software-pipelined so that each
+// SIMD runs one wave's MFMAs while the other wave's VALU work issues:
+//  * 4 math waves own one 16-head block each (up to 64 heads per workgroup). QK(i) runs
+//    v_mfma_f32_16x16x32_f16 with the decoded rows as the A operand and the block's queries
+//    (all 576 dims, pre-scaled by softmax_scale*log2(e), FP16, in registers) as B, so each lane
+//    holds 8 rows of one head; then the online softmax (FP32, base 2, lazily moved running max)
+//    runs in registers and writes FP16 probabilities to LDS.
+//  * 8 producer waves (two per SIMD) gather rows 32 at a time into a 3-slot LDS ring with direct-to-LDS 16-byte
+//    loads (issued three tiles ahead), decode tile i+1 once into FP16 MFMA fragments (VALU, while
+//    the math waves run QK(i)), then run PV(i-1) on their 64 output dims for every head (MFMA,
+//    while the math waves run softmax(i)); V comes from the decoded tile through
+//    ds_read_b64_tr_b16 transposing reads. Empty and out-of-range list entries never reach the
+//    ring: the index list is compacted up front, and padding rows read a zero row.
+// One barrier per 32-row tile; three decoded-tile buffers and two probability buffers.
+//
+// Decoded tile layout ("fragment-major"): for row block rb (16 rows) and K-chunk c (32 dims),
+// 1 KB holds 64 slots of 16 bytes; row r, dims 8*dg..8*dg+7 of the chunk sit in slot
+// 16*dg + (r ^ 4*(dg & 1)). QK fragment reads are then whole 1 KB blocks, and the XOR keeps the
+// transposing V reads free of LDS bank conflicts.
+//
+// Splits write normalised partial outputs (in the producers' register order, 16-byte stores) and
+// their log-sum-exp; combine_kernel merges them in split order (deterministic). With a single
+// split the kernel writes the final output.
+// Workgroup i is placed on XCD i % 8 by the hardware; items are remapped so that the splits of
+// one token are consecutive on one XCD and share its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,11 +44,17 @@
 
 namespace mla {
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+
 constexpr int kTileRows = 32;
-constexpr int kPiecesPerTile = kTileRows * kRowBytes / 16;   // 704 16-byte pieces
-constexpr int kLoadsPerWave = 3;                              // 3 x 4 waves x 64 lanes = 768
-constexpr int kStageBytes = kLoadsPerWave * 4 * 64 * 16;      // 12 KiB per ring slot
-constexpr int kNBuf = 3;
+constexpr int kRawTileBytes = kTileRows * kRowBytes;        // 11264
+constexpr int kRawPieces = kRawTileBytes / 16;                // 704 16-byte pieces
+constexpr int kRawSlots = 3;
+constexpr int kChunks = kQkDim / 32;                          // 18 K-chunks of 32 dims
+constexpr int kFragBytes = 1024;                              // one 16 x 32 FP16 fragment
+constexpr int kDecTileBytes = 2 * kChunks * kFragBytes;       // 36864
+constexpr int kPStride = 80;                                  // bytes per head row of P
+constexpr int kThreads = 768;
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 
 // Source of every load that has no row behind it (padding rows, padding pieces, bad pages).
@@ -69,21 +73,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ half8v q_to_half8(const void* q, int64_t off, bool fp32) {
-  half8v h;
+// Eight query values times `scale`, rounded to FP16.
+__device__ __forceinline__ half8v q_to_half8(const void* q, int64_t off, bool fp32, float scale) {
+  float f[8];
   if (fp32) {
     const float4v a = *(const float4v*)((const float*)q + off);
     const float4v b = *(const float4v*)((const float*)q + off + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { h[i] = (_Float16)a[i]; h[4 + i] = (_Float16)b[i]; }
+    for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
   } else {
     const uint4v u = *(const uint4v*)((const uint16_t*)q + off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      h[2 * i] = (_Float16)__uint_as_float(u[i] << 16);
-      h[2 * i + 1] = (_Float16)__uint_as_float(u[i] & 0xFFFF0000u);
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
     }
   }
+  half8v h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)(f[i] * scale);
   return h;
 }
 
@@ -95,6 +103,7 @@ __device__ __forceinline__ float group4_max(float x) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
 __device__ __forceinline__ float group4_sum(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -106,74 +115,118 @@ __device__ __forceinline__ float4v mfma16(half8v a, half8v b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Byte offset of (row 0..31 of the tile, K-chunk, 8-dim group dg 0..3) in a decoded tile.
+__device__ __forceinline__ int frag_off(int row, int chunk, int dg) {
+  const int rb = row >> 4, r = row & 15;
+  return (rb * kChunks + chunk) * kFragBytes + (((dg << 4) + (r ^ ((dg & 1) << 2))) << 4);
+}
+
+// Direct-to-LDS 16-byte gather: every lane's 16 bytes at `src` land at lds_base + 16*lane.
+// Issued as inline assembly so that the compiler does not order later LDS reads of other
+// buffers behind it (it cannot tell the target apart); completion is tracked explicitly with
+// wait_vmcnt before the barrier that publishes the data.
+__device__ __forceinline__ void gather16_to_lds(const void* src, const uint8_t* lds_base) {
+  // lds_base is the same for every lane of the wave
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const LDS_AS uint8_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ half4v lds_tr16(const uint8_t* p) {
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v*)p);
+  return __builtin_bit_cast(half4v, v);
+}
+
+constexpr int kDecSlots = 3;
+constexpr int kProducers = 8;                                 // producer waves (2 per SIMD)
+
 template <int NH, bool DENSE>
-__global__ __launch_bounds__(256, (NH <= 2) ? 2 : 1) void decode_kernel(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kNBuf][kStageBytes];
-  __shared__ __attribute__((aligned(16))) float4v sred[4][NH][2][64];
-  __shared__ __attribute__((aligned(16))) half8v pbuf[NH][64];
-  __shared__ __attribute__((aligned(16))) float alpha_s[64];
-  __shared__ int32_t rescale_s[4];
-  __shared__ __attribute__((aligned(16))) float mfin[64];
-  __shared__ __attribute__((aligned(16))) float lfin[64];
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t dec[kDecSlots][kDecTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][NH * 16 * kPStride];
+  __shared__ __attribute__((aligned(16))) float alpha_s[2][NH * 16];
+  __shared__ __attribute__((aligned(16))) int32_t flag_s[2][4];
   __shared__ uint32_t rowoff[DENSE ? kMaxDensePages : kMaxSplitRows];
-  __shared__ int32_t wave_cnt[4];
+  __shared__ int32_t cnt_s[4][kProducers];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const bool math = w < 4;
+  const int pw = w - 4;                                  // producer wave index (0..7)
+  const int ptid = tid - 256;                            // producer thread index (0..511)
 
   const int hw = blockIdx.x;
   const int item = (hw & 7) * a.items_per_xcd + (hw >> 3);
   if (item >= a.total_items) return;
   const int split = item % a.n_split;
   const int rest = item / a.n_split;
-  const int hg = a.hg_begin + rest % a.n_hg;
+  const int head0 = a.head_begin + (rest % a.n_hg) * 16 * NH;
   const int tok = rest / a.n_hg;
   const int b = tok / a.q_len, t = tok % a.q_len;
-  const int head0 = hg * 16 * NH;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // ---- rows of this split -------------------------------------------------------------------
-  int n_rows;
+  // ---- math waves: start the query loads of head block w (they overlap the compaction) -------
+  const bool qk_wave = math && w < NH;
+  const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kg;
+  uint4v qraw[kChunks];                       // bf16 queries: one 16-byte load per chunk
+  if (qk_wave && !a.q_fp32) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) qraw[c] = *(const uint4v*)((const uint16_t*)a.q + qrow + 32 * c);
+  }
+
+  // ---- rows of this split (producer waves) --------------------------------------------------
+  int n_rows = 0;
   int p0 = 0;
   if constexpr (!DENSE) {
-    // Compact the valid entries of [e0, e1) into rowoff (16-byte units), in list order.
+    // Compact the valid entries of [e0, e0 + cnt) into rowoff (16-byte units), in list order:
+    // 4 rounds of 512 entries (all index loads first, then all block-table loads), ballot +
+    // mbcnt inside a wave, per-wave counts through LDS.
     const int e0 = split * a.split_rows;
     const int cnt = max(0, min(a.topk, e0 + a.split_rows) - e0);
-    const int per_w = ((cnt + 3) / 4 + 63) & ~63;          // <= 512 entries, 8 rounds of 64
-    const int32_t* idx = a.topk_idx + (int64_t)tok * a.topk + e0;
-    uint32_t offs[8];
-    uint64_t masks[8];
-    int mine = 0;
+    if (!math) {
+      const int32_t* idx = a.topk_idx + (int64_t)tok * a.topk + e0;
+      int jv[4], pg[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = w * per_w + r * 64 + lane;
-      bool ok = false;
-      uint32_t o16 = 0;
-      if (r * 64 < per_w && e < cnt) {
-        const int j = idx[e];
-        if (j >= 0 && j < a.max_pages * kPageRows) {
-          const int pg = bt[j >> 6];
-          if (pg >= 0) {
-            const int64_t off = (int64_t)pg * a.page_stride + (int64_t)(j & 63) * kRowBytes;
-            if (off + kRowBytes <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
-          }
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int e = r * 512 + ptid;
+        jv[r] = (e < cnt) ? idx[e] : -1;
       }
-      masks[r] = __ballot(ok);
-      offs[r] = o16;
-      mine += __popcll(masks[r]);
-    }
-    if (lane == 0) wave_cnt[w] = mine;
-    lds_barrier();
-    int base = 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) base += (v < w) ? wave_cnt[v] : 0;
-    n_rows = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+      for (int r = 0; r < 4; ++r) {
+        const bool in = jv[r] >= 0 && jv[r] < a.max_pages * kPageRows;
+        pg[r] = in ? bt[jv[r] >> 6] : -1;
+      }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(masks[r] >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)masks[r], 0u));
-      if ((masks[r] >> lane) & 1ull) rowoff[base + below] = offs[r];
-      base += __popcll(masks[r]);
+      for (int r = 0; r < 4; ++r) {
+        bool ok = false;
+        uint32_t o16 = 0;
+        if (pg[r] >= 0) {
+          const int64_t off = (int64_t)pg[r] * a.page_stride + (int64_t)(jv[r] & 63) * kRowBytes;
+          if (off + kRowBytes <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
+        }
+        const uint64_t mask = __ballot(ok);
+        if (lane == 0) cnt_s[r][pw] = __popcll(mask);
+        jv[r] = ok ? (int)o16 : -1;               // keep the offset (or -1) for the write below
+      }
+      lds_barrier();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int before = 0, total = 0;
+#pragma unroll
+        for (int v = 0; v < kProducers; ++v) {
+          const int c = cnt_s[r][v];
+          before += (v < pw) ? c : 0;
+          total += c;
+        }
+        const bool ok = jv[r] != -1;
+        const uint64_t mask = __ballot(ok);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (ok) rowoff[n_rows + before + below] = (uint32_t)jv[r];
+        n_rows += total;
+      }
+    } else {
+      lds_barrier();
     }
   } else {
     const int seq = min(a.seq_lens[b], a.max_pages * kPageRows);
@@ -181,229 +234,308 @@ __global__ __launch_bounds__(256, (NH <= 2) ? 2 : 1) void decode_kernel(const De
     p0 = split * a.split_rows;
     n_rows = max(0, min(vis, p0 + a.split_rows) - p0);
     const int n_pages = (n_rows + 63) >> 6;
-    for (int i = tid; i < n_pages; i += 256) {
+    for (int i = tid; i < n_pages; i += kThreads) {
       const int pg = bt[(p0 >> 6) + i];
       const int64_t off = (int64_t)pg * a.page_stride;
       rowoff[i] = (pg < 0) ? kInvalid : (uint32_t)(off >> 4);
     }
+    lds_barrier();                                         // same barrier count as the sparse path
+  }
+  if (tid < 8) flag_s[tid >> 2][tid & 3] = 0;
+  if constexpr (!DENSE) {
+    // the math waves learn the row count from the per-wave counts
+    if (math) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v = 0; v < kProducers; ++v) n_rows += cnt_s[r][v];
+    }
   }
   lds_barrier();
+  const int n_tiles = (n_rows + kTileRows - 1) / kTileRows;
 
-  // ---- query slice (FP16) ---------------------------------------------------------------------
-  half8v qa[NH][5];
-#pragma unroll
-  for (int hb = 0; hb < NH; ++hb) {
-    const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * hb + l16) * kQkDim;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qa[hb][c] = q_to_half8(a.q, qrow + 128 * w + 32 * kg + 8 * c, a.q_fp32);
-    const half8v r = q_to_half8(a.q, qrow + kLatent + 16 * w + 8 * (kg & 1), a.q_fp32);
-    qa[hb][4] = (kg < 2) ? r : half8v{};
-  }
-  // Make the query fragments opaque so the compiler keeps them in registers instead of
-  // re-loading and re-converting them from memory inside the tile loop.
-#pragma unroll
-  for (int hb = 0; hb < NH; ++hb)
-#pragma unroll
-    for (int c = 0; c < 5; ++c) asm volatile("" : "+v"(qa[hb][c]));
+  float* fin_m = (float*)pbuf[0];               // epilogue: per-head running max and sum
+  float* fin_l = fin_m + 64;
 
-  // ---- tile loader --------------------------------------------------------------------------
-  // Each lane moves 16-byte pieces p = (j*4 + w)*64 + lane of the tile (22 pieces per row): the
-  // row offsets are read from LDS together, then every lane issues its loads, with padding
-  // pieces and rows past the end reading the zero row (no divergent branches).
-  auto issue_tile = [&](int tile) {
-    uint8_t* dst = stage[tile % kNBuf];
-    uint32_t o16[kLoadsPerWave];
-    int ri[kLoadsPerWave], piece[kLoadsPerWave];
+  // ---- gathers (issued by the math waves) ---------------------------------------------------
+  // Piece p = k*256 + w*64 + lane (k = 0..2; math wave 3 has no k = 2 piece) of the tile's 704
+  // 16-byte pieces (22 per row). Rows past the end and rows without a valid address read the
+  // zero row, so the ring always holds finite data. The row offsets of a tile are read from LDS
+  // one tile ahead of its gathers.
+  const int nk = (w == 3) ? 2 : 3;
+  auto piece_of = [&](int k, int& prow, int& ppiece) {
+    const int p = min(k * 256 + (w & 3) * 64 + lane, kRawPieces - 1);
+    prow = p / 22;
+    ppiece = p - 22 * prow;
+  };
+  auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int p = min((j * 4 + w) * 64 + lane, kPiecesPerTile - 1);
-      const int r = p / 22;
-      piece[j] = p - r * 22;
-      ri[j] = tile * kTileRows + r;
-      const int rc = min(ri[j], n_rows - 1);
+    for (int k = 0; k < 3; ++k) {
+      int prow, ppiece;
+      piece_of(k, prow, ppiece);
+      const int row = tile * kTileRows + prow;
+      const bool ok = row < n_rows;
       if constexpr (!DENSE) {
-        o16[j] = rowoff[rc];
+        o16[k] = ok ? rowoff[row] : kInvalid;
       } else {
-        const int pos = p0 + rc;
+        const int pos = p0 + (ok ? row : 0);
         const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-        o16[j] = (pb == kInvalid) ? kInvalid : pb + (uint32_t)(pos & 63) * (kRowBytes / 16);
+        const uint32_t o = pb + (uint32_t)(pos & 63) * (kRowBytes / 16);
+        o16[k] = (ok && pb != kInvalid && (int64_t)o * 16 + kRowBytes <= a.cache_bytes) ? o : kInvalid;
       }
     }
+  };
+  auto issue_tile = [&](int tile, const uint32_t (&o16)[3]) {
+    uint8_t* dst = raw[tile % kRawSlots];
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int p = (j * 4 + w) * 64 + lane;
-      bool ok = p < kPiecesPerTile && ri[j] < n_rows && o16[j] != kInvalid;
-      if constexpr (DENSE) ok = ok && (int64_t)o16[j] * 16 + kRowBytes <= a.cache_bytes;
-      const uint8_t* src = ok ? a.cache + (int64_t)o16[j] * 16 + piece[j] * 16
-                              : g_zero_row + piece[j] * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(dst + (j * 4 + w) * 1024), 16, 0, 0);
+    for (int k = 0; k < 3; ++k) {
+      if (k >= nk) break;
+      int prow, ppiece;
+      piece_of(k, prow, ppiece);
+      const uint8_t* src = (o16[k] != kInvalid) ? a.cache + (int64_t)o16[k] * 16 + ppiece * 16
+                                                : g_zero_row + ppiece * 16;
+      gather16_to_lds(src, dst + (k * 256 + w * 64) * 16);
+    }
+  };
+  // Wait until the gathers issued before the last `after` tiles have landed in LDS.
+  auto wait_tiles = [&](int after) {
+    if (nk == 3) {
+      if (after >= 2) wait_vmcnt<6>(); else if (after == 1) wait_vmcnt<3>(); else wait_vmcnt<0>();
+    } else {
+      if (after >= 2) wait_vmcnt<4>(); else if (after == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;       // owner waves: running max (log2 units) and sum
-  float4v o[NH][8];
+  if (math) {
+    // ================================ math waves ================================================
+    // Queries of head block w as 18 FP16 fragments, pre-scaled by softmax_scale * log2(e).
+    half8v qf[kChunks];
 #pragma unroll
-  for (int hb = 0; hb < NH; ++hb)
+    for (int c = 0; c < kChunks; ++c) {
+      float f[8];
+      if (!a.q_fp32) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[hb][c] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  if (w >= NH && lane == 0) rescale_s[w] = 0;       // these waves own no head block
-  const int n_tiles = (n_rows + kTileRows - 1) / kTileRows;
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-
-  for (int i = 0; i < n_tiles; ++i) {
-    if (i + 1 < n_tiles) wait_vmcnt<kLoadsPerWave>(); else wait_vmcnt<0>();
-    lds_barrier();                                   // tile i visible; slot (i-1)%3 free
-    if (i + 2 < n_tiles) issue_tile(i + 2);
-    const uint8_t* tb = stage[i % kNBuf];
-
-    // -- QK: partial S^T over this wave's 144 dims, all heads -----------------------------------
-    half8v kf[2][5];
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(qraw[c][i] << 16);
+          f[2 * i + 1] = __uint_as_float(qraw[c][i] & 0xFFFF0000u);
+        }
+      } else if (qk_wave) {                  // fp32 queries (small launches): load as needed
+        const float4v lo = *(const float4v*)((const float*)a.q + qrow + 32 * c);
+        const float4v hi = *(const float4v*)((const float*)a.q + qrow + 32 * c + 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint8_t* row = tb + (16 * h + l16) * kRowBytes;
-      const uint4v cw = *(const uint4v*)(row + 64 * w + 16 * kg);
-      const uint32_t sc = *(const uint16_t*)(row + kScaleOff + 8 * w + 2 * kg);
-      const uint2v rp = *(const uint2v*)(row + kRopeOff + 16 * w + 8 * (kg & 1));
-      const half2v s0 = scale_pair(sc & 0xFFu), s1 = scale_pair(sc >> 8);
-      kf[h][0] = decode_fp4x8(cw[0], s0);
-      kf[h][1] = decode_fp4x8(cw[1], s0);
-      kf[h][2] = decode_fp4x8(cw[2], s1);
-      kf[h][3] = decode_fp4x8(cw[3], s1);
-      kf[h][4] = (kg < 2) ? decode_fp8x8(rp[0], rp[1]) : half8v{};
+        for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)(f[i] * a.scale_log2);
     }
-    // chunk-major: consecutive MFMAs feed different accumulators (a dependent MFMA would wait
-    // for its predecessor to drain)
-    float4v acc[NH][2];
+    // The query conversion must finish before the first gather: a later wait for the query
+    // loads would otherwise also wait for the gathers, which share the vector-memory counter.
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) { acc[hb][0] = float4v{0.f, 0.f, 0.f, 0.f}; acc[hb][1] = acc[hb][0]; }
+    for (int c = 0; c < kChunks; ++c) asm volatile("" : "+v"(qf[c]));
+    {
+      uint32_t o16[3];
+      tile_offsets(0, o16); issue_tile(0, o16);
+      tile_offsets(1, o16); issue_tile(1, o16);
+      tile_offsets(2, o16); issue_tile(2, o16);
+    }
+    wait_tiles(2);
+    lds_barrier();                            // prologue: tile 0 in LDS
+    wait_tiles(1);
+    lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
+    uint32_t next_o16[3];                     // row offsets of the next tile to gather
+    tile_offsets(3, next_o16);
+    float m_run = -INFINITY, l_run = 0.0f;     // running max (log2 units), partial sum
+    const int kslot = ((kg << 4) + (l16 ^ ((kg & 1) << 2))) << 4;   // QK A-fragment slot
+    for (int i = 0; i <= n_tiles; ++i) {
+      if (qk_wave && i < n_tiles) {
+        const uint8_t* dt = dec[i % kDecSlots];
+        float4v acc[2][2];
 #pragma unroll
-    for (int c = 0; c < 5; ++c)
+        for (int rb = 0; rb < 2; ++rb) { acc[rb][0] = float4v{0.f, 0.f, 0.f, 0.f}; acc[rb][1] = acc[rb][0]; }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-        for (int hb = 0; hb < NH; ++hb) acc[hb][h] = mfma16(kf[h][c], qa[hb][c], acc[hb][h]);
+          for (int rb = 0; rb < 2; ++rb) {
+            const half8v kf = *(const half8v*)(dt + (rb * kChunks + c) * kFragBytes + kslot);
+            acc[rb][c & 1] = mfma16(kf, qf[c], acc[rb][c & 1]);
+          }
+        // Issue order: 8 fragment reads ahead of the MFMAs, then one read per MFMA, so LDS
+        // latency stays hidden behind the matrix work.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {       // every block, the owner's too: no branch
-      sred[w][hb][0][lane] = acc[hb][0];
-      sred[w][hb][1][lane] = acc[hb][1];
+        for (int k = 0; k < 2 * kChunks - 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float4v sc = acc[rb][0] + acc[rb][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = i * kTileRows + 16 * rb + 4 * kg + e;
+            sv[4 * rb + e] = (row < n_rows) ? sc[e] : -INFINITY;
+            mx = fmaxf(mx, sv[4 * rb + e]);
+          }
+        }
+        mx = group4_max(mx);
+        // The running max moves lazily: only when a tile's max exceeds it by more than 2^8, so
+        // the probabilities stay <= 256 (exact range for FP16) and O is rescaled only then.
+        const bool move = mx > m_run + 8.0f;        // also true on the first tile (m_run = -inf)
+        const float m_new = move ? mx : m_run;
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        half4v pf[2];
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+          pf[e >> 2][e & 3] = pv;
+          psum += (float)pv;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        uint8_t* prow_p = pbuf[i & 1] + (16 * w + l16) * kPStride;
+        *(half4v*)(prow_p + 8 * kg) = pf[0];           // rows 4kg..4kg+3
+        *(half4v*)(prow_p + 32 + 8 * kg) = pf[1];      // rows 16+4kg..
+        const uint64_t any = __ballot(move && i > 0);
+        if (lane == 0) flag_s[i & 1][w] = any != 0ull;
+        if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
+      }
+      issue_tile(i + 3, next_o16);
+      tile_offsets(i + 4, next_o16);
+      wait_tiles(1);
+      lds_barrier();
+    }
+    wait_vmcnt<0>();                          // no gather may still target LDS at exit
+    if (qk_wave) {
+      const float lt = group4_sum(l_run);
+      if (kg == 0) { fin_m[16 * w + l16] = m_run; fin_l[16 * w + l16] = lt; }
     }
     lds_barrier();
+  } else {
+    // ================================ producer waves ============================================
+    // Decode: lane (pw, kg, l16) decodes code piece p = 4*(pw&3) + kg (32 latent dims =
+    // K-chunk p) of row 16*(pw>>2) + l16; waves 0..3 also decode one rope group of 8 dims.
+    const int dp = 4 * (pw & 3) + kg;
+    const int drow = 16 * (pw >> 2) + l16;
+    const int ru = (pw & 3) * 64 + lane;                  // rope unit (waves 0..3)
+    const int rrow = ru & 31, rg = ru >> 5;
+    struct DecodeIn { uint4v cw; uint32_t sc; uint2v rp; };
+    auto decode_load = [&](int tile) {
+      const uint8_t* src = raw[tile % kRawSlots];
+      const uint8_t* row = src + drow * kRowBytes;
+      DecodeIn d;
+      d.cw = *(const uint4v*)(row + 16 * dp);
+      d.sc = *(const uint16_t*)(row + kScaleOff + 2 * dp);
+      d.rp = (pw < 4) ? *(const uint2v*)(src + rrow * kRowBytes + kRopeOff + 8 * rg) : uint2v{0u, 0u};
+      return d;
+    };
+    auto decode_store = [&](int tile, const DecodeIn& d) {
+      uint8_t* dst = dec[tile % kDecSlots];
+      const half2v s01 = fp8x2_to_half2<false>(d.sc);
+      const half2v s0 = half2v{s01[0], s01[0]}, s1 = half2v{s01[1], s01[1]};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *(half8v*)(dst + frag_off(drow, dp, k)) = decode_fp4x8(d.cw[k], k < 2 ? s0 : s1);
+      if (pw < 4) *(half8v*)(dst + frag_off(rrow, 16 + (rg >> 2), rg & 3)) = decode_fp8x8(d.rp[0], d.rp[1]);
+    };
+    auto decode_tile = [&](int tile) { decode_store(tile, decode_load(tile)); };
 
-    // -- online softmax on the owning wave ------------------------------------------------------
-    if (w < NH) {
-      float4v s0 = sred[0][w][0][lane], s1 = sred[0][w][1][lane];
+    // Output accumulators of dims 64*pw + 16*n + l16, heads 16*hb + 4*kg + e.
+    float4v o[NH][4];
 #pragma unroll
-      for (int src = 1; src < 4; ++src) { s0 += sred[src][w][0][lane]; s1 += sred[src][w][1][lane]; }
-      float sv[8];
-      float mx = -INFINITY;
+    for (int hb = 0; hb < NH; ++hb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ra = i * kTileRows + 4 * kg + r, rb = ra + 16;
-        sv[r] = (ra < n_rows) ? s0[r] * a.scale_log2 : -INFINITY;
-        sv[4 + r] = (rb < n_rows) ? s1[r] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, fmaxf(sv[r], sv[4 + r]));
+      for (int n = 0; n < 4; ++n) o[hb][n] = float4v{0.f, 0.f, 0.f, 0.f};
+    lds_barrier();                            // prologue: tile 0 in LDS
+    if (n_tiles > 0) decode_tile(0);
+    lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
+    // Transposing-read offsets (V operand of PV): the lane supplies 4 dims
+    // (16*n + 4*(l16&3) ..) of row 8*kg + (l16>>2) (+4 for the second read).
+    const int vq = l16 >> 2, va = l16 & 3;
+    const int vrow0 = 8 * kg + vq;
+    for (int i = 0; i <= n_tiles; ++i) {
+      // raw bytes of tile i+1 first: their LDS latency hides behind PV(i-1)
+      const bool dec_next = i + 1 < n_tiles;
+      DecodeIn din;
+      if (dec_next) din = decode_load(i + 1);
+      if (i >= 1) {
+        // PV(i-1): rescale by alpha(i-1) where the running max moved, then O += P V.
+        const int j = i - 1;
+        const uint8_t* dt = dec[j % kDecSlots];
+        const int4 fl = *(const int4*)flag_s[j & 1];
+        if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+#pragma unroll
+          for (int hb = 0; hb < NH; ++hb) {
+            const int f = (hb == 0) ? fl.x : (hb == 1) ? fl.y : (hb == 2) ? fl.z : fl.w;
+            if (f) {
+              const float4v al = *(const float4v*)&alpha_s[j & 1][16 * hb + 4 * kg];
+#pragma unroll
+              for (int n = 0; n < 4; ++n) o[hb][n] *= al;
+            }
+          }
+        }
+        half8v pa[NH];
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb)
+          pa[hb] = *(const half8v*)(pbuf[j & 1] + (16 * hb + l16) * kPStride + 16 * kg);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int ng = 4 * pw + n;
+          const int dg = 2 * (ng & 1) + (va >> 1);
+          const int off0 = frag_off(vrow0, ng >> 1, dg) + 8 * (va & 1);
+          const int off1 = frag_off(vrow0 + 4, ng >> 1, dg) + 8 * (va & 1);
+          const half4v v0 = lds_tr16(dt + off0);
+          const half4v v1 = lds_tr16(dt + off1);
+          const half8v vb = half8v{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int hb = 0; hb < NH; ++hb) o[hb][n] = mfma16(pa[hb], vb, o[hb][n]);
+        }
       }
-      mx = group4_max(mx);
-      // The running max moves lazily: only when a tile's max exceeds it by more than 2^8, so the
-      // probabilities stay <= 256 (exact range for FP16) and O is rescaled only on those tiles.
-      const bool move = mx > m_run + 8.0f;        // also true on the first tile (m_run = -inf)
-      const float m_new = move ? mx : m_run;
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      half8v pf;
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
-        pf[e] = p;
-        psum += (float)p;
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      const uint64_t any = __ballot(move && i > 0);
-      if (lane == 0) rescale_s[w] = any != 0ull;
-      pbuf[w][lane] = pf;
-      if (kg == 0) alpha_s[16 * w + l16] = alpha;
+      if (dec_next) decode_store(i + 1, din);
+      lds_barrier();
     }
-    lds_barrier();
+    lds_barrier();                              // fin_m / fin_l written by the math waves
 
-    // -- PV: this wave's 128 output dims, all heads ----------------------------------------------
-    half8v pfr[NH];
+    // ---- normalise and write ----------------------------------------------------------------
+    const bool final_out = (a.n_split == 1);
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) pfr[hb] = pbuf[hb][lane];
-    const bool rescale = (rescale_s[0] | rescale_s[1] | rescale_s[2] | rescale_s[3]) != 0;
-    // V fragments: 8 tokens of one dim per lane (the P fragment's token slots), decoded while the
-    // P fragments are in flight.
-    uint32_t D[8], SB[8];
+    for (int hb = 0; hb < NH; ++hb) {
+      const float4v mm = *(const float4v*)&fin_m[16 * hb + 4 * kg];
+      const float4v ll = *(const float4v*)&fin_l[16 * hb + 4 * kg];
+      float4v inv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int te = (e < 4) ? 4 * kg + e : 16 + 4 * kg + (e - 4);
-      const uint8_t* row = tb + te * kRowBytes;
-      D[e] = *(const uint32_t*)(row + 64 * w + 4 * l16);
-      SB[e] = row[kScaleOff + 8 * w + (l16 >> 1)];
-    }
-    half8v v[8];
+      for (int e = 0; e < 4; ++e) inv[e] = ll[e] > 0.0f ? 1.0f / ll[e] : 0.0f;
+      const int hbg = (head0 >> 4) + hb;                  // global 16-head block
+      if (final_out) {
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const uint32_t da = D[2 * pr], db = D[2 * pr + 1];
-      const uint32_t ze = (da & 0x0F0F0F0Fu) | ((db & 0x0F0F0F0Fu) << 4);
-      const uint32_t zo = ((da >> 4) & 0x0F0F0F0Fu) | (db & 0xF0F0F0F0u);
-      const half2v sab = fp8x2_to_half2<false>(SB[2 * pr] | (SB[2 * pr + 1] << 8));
-      half2v x;
-      x = fp4x2_to_half2<0>(ze) * sab; v[0][2 * pr] = x[0]; v[0][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<0>(zo) * sab; v[1][2 * pr] = x[0]; v[1][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<1>(ze) * sab; v[2][2 * pr] = x[0]; v[2][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<1>(zo) * sab; v[3][2 * pr] = x[0]; v[3][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<2>(ze) * sab; v[4][2 * pr] = x[0]; v[4][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<2>(zo) * sab; v[5][2 * pr] = x[0]; v[5][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<3>(ze) * sab; v[6][2 * pr] = x[0]; v[6][2 * pr + 1] = x[1];
-      x = fp4x2_to_half2<3>(zo) * sab; v[7][2 * pr] = x[0]; v[7][2 * pr + 1] = x[1];
-    }
-    if (rescale) {
+        for (int e = 0; e < 4; ++e) {
+          float* dst = a.out + ((int64_t)tok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
 #pragma unroll
-      for (int hb = 0; hb < NH; ++hb) {
-        const float4v al = *(const float4v*)&alpha_s[16 * hb + 4 * kg];
+          for (int n = 0; n < 4; ++n) dst[16 * n] = o[hb][n][e] * inv[e];
+        }
+      } else {
+        // partial in register order: [token][split][16-head block][dim block 0..31][lane][4 heads]
+        float* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[hb][c] *= al;
+        for (int n = 0; n < 4; ++n) *(float4v*)(dst + 256 * n) = o[hb][n] * inv;
       }
-    }
+      if (pw == 0 && l16 == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int hb = 0; hb < NH; ++hb) o[hb][c] = mfma16(pfr[hb], v[c], o[hb][c]);
-  }
-
-  // ---- normalise and write ------------------------------------------------------------------
-  if (w < NH) {
-    const float lt = group4_sum(l_run);
-    if (kg == 0) { mfin[16 * w + l16] = m_run; lfin[16 * w + l16] = lt; }
-  }
-  lds_barrier();
-  const bool final_out = (a.n_split == 1);
-#pragma unroll
-  for (int hb = 0; hb < NH; ++hb) {
-    const float4v mm = *(const float4v*)&mfin[16 * hb + 4 * kg];
-    const float4v ll = *(const float4v*)&lfin[16 * hb + 4 * kg];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float inv = ll[r] > 0.0f ? 1.0f / ll[r] : 0.0f;
-      const int head = head0 + 16 * hb + 4 * kg + r;
-      float* dst = final_out
-          ? a.out + ((int64_t)tok * a.H + head) * kLatent
-          : a.ws_o + (((int64_t)tok * a.n_split + split) * a.H + head) * kLatent;
-      dst += 128 * w + 8 * l16;
-      const float4v lo = float4v{o[hb][0][r], o[hb][1][r], o[hb][2][r], o[hb][3][r]} * inv;
-      const float4v hi = float4v{o[hb][4][r], o[hb][5][r], o[hb][6][r], o[hb][7][r]} * inv;
-      *(float4v*)dst = lo;
-      *(float4v*)(dst + 4) = hi;
-      if (w == 0 && l16 == 0) {
-        const float lse_v = ll[r] > 0.0f
-            ? (mm[r] + __builtin_amdgcn_logf(ll[r])) * 0.69314718055994530942f : -INFINITY;
-        if (final_out) {
-          if (a.lse) a.lse[(int64_t)tok * a.H + head] = lse_v;
-        } else {
-          a.ws_lse[((int64_t)tok * a.n_split + split) * a.H + head] = lse_v;
+        for (int e = 0; e < 4; ++e) {
+          const int head = 16 * hbg + 4 * kg + e;
+          const float lse_v = ll[e] > 0.0f
+              ? (mm[e] + __builtin_amdgcn_logf(ll[e])) * 0.69314718055994530942f : -INFINITY;
+          if (final_out) {
+            if (a.lse) a.lse[(int64_t)tok * a.H + head] = lse_v;
+          } else {
+            a.ws_lse[((int64_t)tok * a.n_split + split) * a.H + head] = lse_v;
+          }
         }
       }
     }
@@ -412,46 +544,77 @@ __global__ __launch_bounds__(256, (NH <= 2) ? 2 : 1) void decode_kernel(const De
 
 // Merge the n_split partial (o_s, lse_s) of each (token, head) in split order:
 // M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
+// A thread owns one dim of 4 heads, the 16-byte unit the decode kernel stored; splits are taken
+// 8 at a time with every load of a chunk issued before its first use.
+constexpr int kCombineChunk = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int32_t S,
                                                       const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse,
                                                       int32_t per_xcd, int32_t total) {
+  // block = (token, 16-head block, 4 dim blocks); thread = (dim block, lane)
   const int hw = blockIdx.x;
   const int L = (hw & 7) * per_xcd + (hw >> 3);
   if (L >= total) return;
-  const int quads = H / 4;
-  const int tok = L / quads;
-  const int head = (L % quads) * 4 + (threadIdx.x >> 6);
-  const int d = (threadIdx.x & 63) * 8;
+  const int nhb = H >> 4;
+  const int tok = L / (nhb * 8);
+  const int r = L % (nhb * 8);
+  const int hb = r >> 3;
+  const int ng = (r & 7) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
+  const int head = 16 * hb + 4 * kg;                      // heads head..head+3
+  const int64_t split_stride = (int64_t)H * kLatent;
+  const float* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 32 + ng) * 64 + lane) * 4;
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(int64_t)s * H]);
-  float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  float wsum = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lp[(int64_t)s * H];
-      const float wgt = (ls == -INFINITY) ? 0.0f
-                                          : __builtin_amdgcn_exp2f((ls - M) * 1.4426950408889634f);
-      const float* op = ws_o + (((int64_t)tok * S + s) * H + head) * kLatent + d;
-      acc0 += wgt * *(const float4v*)op;
-      acc1 += wgt * *(const float4v*)(op + 4);
-      wsum += wgt;
-    }
+  float4v M = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+    float4v v[kCombineChunk];
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j)
+      v[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)(s0 + j) * H)
+                          : float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], v[j][e]);
   }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  float* dst = out + ((int64_t)tok * H + head) * kLatent + d;
-  *(float4v*)dst = acc0 * inv;
-  *(float4v*)(dst + 4) = acc1 * inv;
-  if (lse && (threadIdx.x & 63) == 0)
-    lse[(int64_t)tok * H + head] =
-        (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(wsum) * 0.69314718055994530942f;
+  float4v acc = float4v{0.f, 0.f, 0.f, 0.f}, wsum = acc;
+  for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+    float4v ls[kCombineChunk], ov[kCombineChunk];
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j) {
+      const int s = min(s0 + j, S - 1);
+      ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H)
+                           : float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      ov[j] = *(const float4v*)(op + s * split_stride);
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float wgt = (ls[j][e] == -INFINITY) ? 0.0f
+                                                  : __builtin_amdgcn_exp2f((ls[j][e] - M[e]) * 1.4426950408889634f);
+        acc[e] += wgt * ov[j][e];
+        wsum[e] += wgt;
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
+    out[((int64_t)tok * H + head + e) * kLatent + 16 * ng + l16] = acc[e] * inv;
+  }
+  if (lse && ng == 0 && l16 == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      lse[(int64_t)tok * H + head + e] =
+          (M[e] == -INFINITY) ? -INFINITY : M[e] + __builtin_amdgcn_logf(wsum[e]) * 0.69314718055994530942f;
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream) {
-  const dim3 grid((unsigned)a.items_per_xcd * 8), block(256);
+  const dim3 grid((unsigned)a.items_per_xcd * 8), block(kThreads);
 #define MLA_LAUNCH(NHV, DV) \
   hipLaunchKernelGGL((decode_kernel<NHV, DV>), grid, block, 0, stream, a)
   switch (nh * 2 + (dense ? 1 : 0)) {
@@ -471,7 +634,7 @@ hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t st
 
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const float* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
-  const int32_t total = T * (H / 4);
+  const int32_t total = T * (H / 16) * 8;
   const int32_t per_xcd = (total + 7) / 8;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
                      n_split, ws_o, ws_lse, out, lse, per_xcd, total);

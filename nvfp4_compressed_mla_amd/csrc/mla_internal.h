@@ -22,8 +22,8 @@ struct DecodeArgs {
   float scale_log2;         // softmax_scale * log2(e)
   int32_t n_split;          // row splits per (token, head group)
   int32_t split_rows;       // list entries (sparse) or positions (dense) per split, multiple of 64
-  int32_t hg_begin;         // first 64-head group handled by this launch
-  int32_t n_hg;             // head groups handled by this launch
+  int32_t head_begin;       // first head handled by this launch
+  int32_t n_hg;             // head groups (of 16*nh heads) handled by this launch
   int32_t total_items;      // T * n_hg * n_split
   int32_t items_per_xcd;    // ceil(total_items / 8)
   float* out;               // [T, H, 512] (n_split == 1)
@@ -43,7 +43,7 @@ hipError_t launch_quantize_append(const void* latent, int64_t latent_stride, con
 hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_t cache_bytes,
                                   const int64_t* slots, int64_t n, float* out, hipStream_t stream);
 
-// nh = heads per group / 16 (1..4); dense selects implicit positions.
+// nh = heads per workgroup / 16 (1..4); dense selects implicit positions.
 hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream);
 
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const float* ws_o,
