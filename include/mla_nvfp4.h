@@ -81,8 +81,9 @@ mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stri
                                      int64_t cache_bytes, hipStream_t stream);
 
 /* Bytes of workspace mla_sparse_decode / mla_dense_decode need for `num_splits` row splits of
- * `num_tokens` (= B*q_len) query tokens with H heads: num_tokens*num_splits*H*(512+1)*4 rounded
- * up to 256. Zero when num_splits <= 1 (no partials are kept). */
+ * `num_tokens` (= B*q_len) query tokens with H heads: num_tokens*num_splits*H*(512*2 + 4) rounded
+ * up to 256 (each split keeps its normalised partial output in FP16 and its log-sum-exp in FP32;
+ * the merge runs in FP32). Zero when num_splits <= 1 (no partials are kept). */
 size_t mla_decode_workspace_size(int32_t num_tokens, int32_t H, int32_t num_splits);
 
 /* Number of row splits mla_sparse_decode will use for this shape when `max_splits` = 0 (auto,

@@ -52,7 +52,8 @@ int waves_capacity(int32_t) { return kComputeUnits; }
 
 size_t ws_bytes(int64_t T, int64_t H, int64_t S) {
   if (S <= 1) return 0;
-  const size_t b = (size_t)(T * S * H * (MLA_LATENT_DIM + 1)) * sizeof(float);
+  // FP16 partial outputs (512 per head) followed by FP32 partial log-sum-exp (1 per head)
+  const size_t b = (size_t)(T * S * H) * (MLA_LATENT_DIM * 2 + sizeof(float));
   return (b + 255) & ~(size_t)255;
 }
 
@@ -232,8 +233,8 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_ca
   a.out = out;
   a.lse = lse;
   if (num_splits > 1) {
-    a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + T * num_splits * H * MLA_LATENT_DIM;
+    a.ws_o = (_Float16*)workspace;
+    a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
   }
   return run_decode(a, H, false, stream);
 }
@@ -273,8 +274,8 @@ mla_status mla_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cac
   a.out = out;
   a.lse = lse;
   if (num_splits > 1) {
-    a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + T * num_splits * H * MLA_LATENT_DIM;
+    a.ws_o = (_Float16*)workspace;
+    a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
   }
   return run_decode(a, H, true, stream);
 }

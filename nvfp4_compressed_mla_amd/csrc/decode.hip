@@ -168,10 +168,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // ---- math waves: start the query loads of head block w (they overlap the compaction) -------
   const bool qk_wave = math && w < NH;
   const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kg;
-  uint4v qraw[kChunks];                       // bf16 queries: one 16-byte load per chunk
-  if (qk_wave && !a.q_fp32) {
+  half8v qf[kChunks];                         // queries as 18 FP16 fragments (math waves)
+  if (math) {
+    // Pre-scaled by softmax_scale * log2(e). Converted here, while the producer waves compact
+    // the index list.
+    uint4v qraw[kChunks];                     // bf16 queries: one 16-byte load per chunk
+    if (qk_wave && !a.q_fp32) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) qraw[c] = *(const uint4v*)((const uint16_t*)a.q + qrow + 32 * c);
+      for (int c = 0; c < kChunks; ++c) qraw[c] = *(const uint4v*)((const uint16_t*)a.q + qrow + 32 * c);
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      float f[8];
+      if (!a.q_fp32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(qraw[c][i] << 16);
+          f[2 * i + 1] = __uint_as_float(qraw[c][i] & 0xFFFF0000u);
+        }
+      } else if (qk_wave) {                  // fp32 queries (small launches): load as needed
+        const float4v lo = *(const float4v*)((const float*)a.q + qrow + 32 * c);
+        const float4v hi = *(const float4v*)((const float*)a.q + qrow + 32 * c + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)(f[i] * a.scale_log2);
+    }
   }
 
   // ---- rows of this split (producer waves) --------------------------------------------------
@@ -185,16 +211,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     const int cnt = max(0, min(a.topk, e0 + a.split_rows) - e0);
     if (!math) {
       const int32_t* idx = a.topk_idx + (int64_t)tok * a.topk + e0;
-      int jv[4], pg[4];
+      // Branch-free loads (clamped addresses, results selected afterwards) so that all index
+      // loads are in flight together, then all block-table loads.
+      int jv[4] = {-1, -1, -1, -1}, pg[4] = {-1, -1, -1, -1};
+      if (cnt > 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = r * 512 + ptid;
-        jv[r] = (e < cnt) ? idx[e] : -1;
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int e = r * 512 + ptid;
+          const int v = idx[min(e, cnt - 1)];
+          jv[r] = (e < cnt) ? v : -1;
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool in = jv[r] >= 0 && jv[r] < a.max_pages * kPageRows;
-        pg[r] = in ? bt[jv[r] >> 6] : -1;
+        for (int r = 0; r < 4; ++r) {
+          const bool in = jv[r] >= 0 && jv[r] < a.max_pages * kPageRows;
+          const int v = bt[in ? (jv[r] >> 6) : 0];
+          pg[r] = in ? v : -1;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -263,17 +295,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // zero row, so the ring always holds finite data. The row offsets of a tile are read from LDS
   // one tile ahead of its gathers.
   const int nk = (w == 3) ? 2 : 3;
-  auto piece_of = [&](int k, int& prow, int& ppiece) {
+  uint32_t pk[3];                              // (row in tile << 16) | byte offset in the row
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
     const int p = min(k * 256 + (w & 3) * 64 + lane, kRawPieces - 1);
-    prow = p / 22;
-    ppiece = p - 22 * prow;
-  };
+    pk[k] = ((uint32_t)(p / 22) << 16) | (uint32_t)((p % 22) * 16);
+  }
   auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      int prow, ppiece;
-      piece_of(k, prow, ppiece);
-      const int row = tile * kTileRows + prow;
+      const int row = tile * kTileRows + (int)(pk[k] >> 16);
       const bool ok = row < n_rows;
       if constexpr (!DENSE) {
         o16[k] = ok ? rowoff[row] : kInvalid;
@@ -290,10 +321,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       if (k >= nk) break;
-      int prow, ppiece;
-      piece_of(k, prow, ppiece);
-      const uint8_t* src = (o16[k] != kInvalid) ? a.cache + (int64_t)o16[k] * 16 + ppiece * 16
-                                                : g_zero_row + ppiece * 16;
+      const uint32_t pb = pk[k] & 0xFFFFu;
+      const uint8_t* src = (o16[k] != kInvalid) ? a.cache + (int64_t)o16[k] * 16 + pb : g_zero_row + pb;
       gather16_to_lds(src, dst + (k * 256 + w * 64) * 16);
     }
   };
@@ -308,29 +337,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   if (math) {
     // ================================ math waves ================================================
-    // Queries of head block w as 18 FP16 fragments, pre-scaled by softmax_scale * log2(e).
-    half8v qf[kChunks];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      float f[8];
-      if (!a.q_fp32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = __uint_as_float(qraw[c][i] << 16);
-          f[2 * i + 1] = __uint_as_float(qraw[c][i] & 0xFFFF0000u);
-        }
-      } else if (qk_wave) {                  // fp32 queries (small launches): load as needed
-        const float4v lo = *(const float4v*)((const float*)a.q + qrow + 32 * c);
-        const float4v hi = *(const float4v*)((const float*)a.q + qrow + 32 * c + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)(f[i] * a.scale_log2);
-    }
     // The query conversion must finish before the first gather: a later wait for the query
     // loads would otherwise also wait for the gathers, which share the vector-memory counter.
 #pragma unroll
@@ -371,6 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        uint32_t cur_o16[3] = {next_o16[0], next_o16[1], next_o16[2]};
+        tile_offsets(i + 4, next_o16);                // their LDS latency hides behind the softmax
         float sv[8];
         float mx = -INFINITY;
 #pragma unroll
@@ -405,9 +413,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         const uint64_t any = __ballot(move && i > 0);
         if (lane == 0) flag_s[i & 1][w] = any != 0ull;
         if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
+        issue_tile(i + 3, cur_o16);
       }
-      issue_tile(i + 3, next_o16);
-      tile_offsets(i + 4, next_o16);
+      if (!(qk_wave && i < n_tiles)) { issue_tile(i + 3, next_o16); tile_offsets(i + 4, next_o16); }
       wait_tiles(1);
       lds_barrier();
     }
@@ -520,10 +528,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int n = 0; n < 4; ++n) dst[16 * n] = o[hb][n][e] * inv[e];
         }
       } else {
-        // partial in register order: [token][split][16-head block][dim block 0..31][lane][4 heads]
-        float* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+        // FP16 partial in register order: [token][split][16-head block][dim block][lane][4 heads]
+        _Float16* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) *(float4v*)(dst + 256 * n) = o[hb][n] * inv;
+        for (int n = 0; n < 4; ++n) {
+          const float4v v = o[hb][n] * inv;
+          *(half4v*)(dst + 256 * n) = half4v{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        }
       }
       if (pw == 0 && l16 == 0) {
 #pragma unroll
@@ -544,12 +555,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
 // Merge the n_split partial (o_s, lse_s) of each (token, head) in split order:
 // M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
-// A thread owns one dim of 4 heads, the 16-byte unit the decode kernel stored; splits are taken
+// A thread owns one dim of 4 heads, the 8-byte FP16 unit the decode kernel stored; splits are taken
 // 8 at a time with every load of a chunk issued before its first use.
 constexpr int kCombineChunk = 8;
 
 __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int32_t S,
-                                                      const float* __restrict__ ws_o,
+                                                      const _Float16* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse,
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   const int lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
   const int head = 16 * hb + 4 * kg;                      // heads head..head+3
   const int64_t split_stride = (int64_t)H * kLatent;
-  const float* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 32 + ng) * 64 + lane) * 4;
+  const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 32 + ng) * 64 + lane) * 4;
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
   float4v M = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
@@ -588,7 +599,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
       const int s = min(s0 + j, S - 1);
       ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H)
                            : float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      ov[j] = *(const float4v*)(op + s * split_stride);
+      const half4v hv = *(const half4v*)(op + s * split_stride);
+      ov[j] = float4v{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
     }
 #pragma unroll
     for (int j = 0; j < kCombineChunk; ++j)
@@ -632,7 +644,7 @@ hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const float* ws_o,
+hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
   const int32_t total = T * (H / 16) * 8;
   const int32_t per_xcd = (total + 7) / 8;

@@ -28,7 +28,7 @@ struct DecodeArgs {
   int32_t items_per_xcd;    // ceil(total_items / 8)
   float* out;               // [T, H, 512] (n_split == 1)
   float* lse;               // [T, H] or null (n_split == 1)
-  float* ws_o;              // [T, n_split, H, 512] partial outputs (n_split > 1)
+  _Float16* ws_o;           // [T, n_split, H/16, 32, 64, 4] FP16 partial outputs (n_split > 1)
   float* ws_lse;            // [T, n_split, H] partial log-sum-exp (natural log)
 };
 
@@ -46,7 +46,7 @@ hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_
 // nh = heads per workgroup / 16 (1..4); dense selects implicit positions.
 hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream);
 
-hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const float* ws_o,
+hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream);
 
 }  // namespace mla

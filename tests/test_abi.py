@@ -128,5 +128,5 @@ def test_launch_shaping(lib):
     assert lib.mla_sparse_decode_num_splits(1, 64, 2048, 100) == 32
     assert lib.mla_dense_decode_num_splits(2336, 4096) == 37
     assert lib.mla_decode_workspace_size(32, 64, 1) == 0
-    assert lib.mla_decode_workspace_size(32, 64, 8) == 32 * 8 * 64 * 513 * 4
+    assert lib.mla_decode_workspace_size(32, 64, 8) == 32 * 8 * 64 * (512 * 2 + 4)
     assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
