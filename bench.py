@@ -42,8 +42,8 @@ def log(msg):
 
 
 def head_group_blocks(H: int) -> int:
-    """16-head blocks per decode workgroup (the library's head grouping: 32 heads when H % 32 == 0)."""
-    return 2 if H % 32 == 0 else 1
+    """16-head blocks per decode workgroup of the first launch (the library groups up to 64 heads)."""
+    return min(4, H // 16)
 
 
 def kernel_source_hash() -> str:
