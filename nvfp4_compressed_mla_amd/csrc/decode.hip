@@ -13,7 +13,7 @@
 // SIMD runs one wave's MFMAs while the other wave's VALU work issues:
 //  * 4 math waves own one 16-head block each (up to 64 heads per workgroup). QK(i) runs
 //    v_mfma_f32_16x16x32_f16 with the decoded rows as the A operand and the block's queries
-//    (all 576 dims, pre-scaled by softmax_scale*log2(e), FP16, in registers) as B, so each lane
+//    (all 576 dims, FP16, in registers) as B, so each lane
 //    holds 8 rows of one head; then the online softmax (FP32, base 2, lazily moved running max)
 //    runs in registers and writes FP16 probabilities to LDS.
 //  * 8 producer waves (two per SIMD) gather rows 32 at a time into a 3-slot LDS ring with direct-to-LDS 16-byte
@@ -170,8 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kg;
   half8v qf[kChunks];                         // queries as 18 FP16 fragments (math waves)
   if (math) {
-    // Pre-scaled by softmax_scale * log2(e). Converted here, while the producer waves compact
-    // the index list.
+    // Converted here (FP16; softmax_scale * log2(e) is applied to the scores), while the
+    // producer waves compact the index list.
     uint4v qraw[kChunks];                     // bf16 queries: one 16-byte load per chunk
     if (qk_wave && !a.q_fp32) {
 #pragma unroll
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         for (int i = 0; i < 8; ++i) f[i] = 0.0f;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)(f[i] * a.scale_log2);
+      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)f[i];
     }
   }
 
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = i * kTileRows + 16 * rb + 4 * kg + e;
-            sv[4 * rb + e] = (row < n_rows) ? sc[e] : -INFINITY;
+            sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[4 * rb + e]);
           }
         }
