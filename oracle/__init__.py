@@ -20,10 +20,11 @@ Sources followed (cited by page title and section, as printed on the page):
 * OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element encoding (bias 1, values 0, 0.5, 1, 1.5,
   2, 3, 4, 6).
 
-Modules: ``nvfp4`` (element and row codec), ``cache`` (paged row addressing), ``attention``
-(fp64 sparse / dense absorbed-MLA decode and the split log-sum-exp merge).
+Modules: ``nvfp4`` (element and row codec), ``fp8`` (the 576-byte FP8 baseline row and the staged
+NVFP4 -> FP8 conversion), ``cache`` (paged row addressing), ``attention`` (fp64 sparse / dense
+absorbed-MLA decode and the split log-sum-exp merge).
 
 Parity pins live in ``tests/test_oracle_*.py`` (run with ``-m "not gpu"``).
 """
 
-from . import nvfp4, cache, attention  # noqa: F401
+from . import nvfp4, fp8, cache, attention  # noqa: F401

@@ -29,7 +29,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .nvfp4 import LATENT_DIM, ROPE_DIM, dequantize_rows
+from .nvfp4 import LATENT_DIM, ROPE_DIM, ROW_BYTES, dequantize_rows
+from .fp8 import FP8_ROW_BYTES, dequantize_rows_fp8
 from .cache import read_rows
 
 QK_DIM = LATENT_DIM + ROPE_DIM    # 576
@@ -55,17 +56,23 @@ def attend(q_heads, keys, values, softmax_scale):
 
 
 def rows_to_kv(rows):
-    """Dequantize 352-byte rows into (K [n,576], V [n,512]) fp64."""
-    lat, rope = dequantize_rows(rows)
+    """Dequantize 352-byte NVFP4 rows (or 576-byte FP8 rows) into (K [n,576], V [n,512]) fp64."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    if rows.shape[1] == FP8_ROW_BYTES:
+        lat, rope = dequantize_rows_fp8(rows)
+    else:
+        lat, rope = dequantize_rows(rows)
     return np.concatenate([lat, rope], axis=1), lat
 
 
-def sparse_decode(q, cache, page_stride, block_table, topk_idx, softmax_scale, tokens=None):
+def sparse_decode(q, cache, page_stride, block_table, topk_idx, softmax_scale, tokens=None,
+                  row_bytes=ROW_BYTES):
     """Sparse decode: each query token attends to the rows its index list selects.
 
     q [B, q_len, H, 576] (real values), cache uint8 flat bytes, block_table int [B, max_pages],
     topk_idx int [B, q_len, k] (logical positions, -1 = empty).
     ``tokens``: optional list of (b, t) pairs to compute; the other outputs are left as NaN.
+    ``row_bytes``: 352 for the NVFP4 cache, 576 for the FP8 baseline cache.
     Returns out fp64 [B, q_len, H, 512], lse fp64 [B, q_len, H].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -77,7 +84,7 @@ def sparse_decode(q, cache, page_stride, block_table, topk_idx, softmax_scale, t
     todo = tokens if tokens is not None else [(b, t) for b in range(b_n) for t in range(q_len)]
     for b, t in todo:
         sel = [int(j) for j in np.asarray(topk_idx[b, t]).tolist() if j >= 0]
-        rows = read_rows(cache, page_stride, block_table[b], sel)
+        rows = read_rows(cache, page_stride, block_table[b], sel, row_bytes)
         keys, values = rows_to_kv(rows)
         out[b, t], lse[b, t] = attend(q[b, t], keys, values, softmax_scale)
     return out, lse

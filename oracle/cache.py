@@ -1,4 +1,4 @@
-"""Paged cache addressing for 352-byte rows (plain byte arithmetic, no blocking).
+"""Paged cache addressing for 352-byte NVFP4 rows (and 576-byte FP8 rows), plain byte arithmetic.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``); never imported by the product path.
 
@@ -8,7 +8,7 @@ is therefore addressed through a byte stride (``page_stride``) that is at least 
 the block-major case, covers all layers of the block.
 
 Readings: a physical slot is ``page * 64 + offset``; its row starts at byte
-``page * page_stride + offset * 352``. A logical position ``j`` of request ``b`` lives in page
+``page * page_stride + offset * 352`` (``offset * 576`` for FP8 rows). A logical position ``j`` of request ``b`` lives in page
 ``block_table[b][j // 64]`` at offset ``j % 64``. Slot ``-1`` means "do not write".
 """
 
@@ -21,32 +21,38 @@ from .nvfp4 import ROW_BYTES
 PAGE_ROWS = 64
 
 
-def row_offset(slot: int, page_stride: int) -> int:
+def row_offset(slot: int, page_stride: int, row_bytes: int = ROW_BYTES) -> int:
     """Byte offset of physical slot ``slot`` in a cache whose pages are ``page_stride`` bytes."""
     page, off = divmod(int(slot), PAGE_ROWS)
-    return page * int(page_stride) + off * ROW_BYTES
+    return page * int(page_stride) + off * int(row_bytes)
 
 
 def write_rows(cache: np.ndarray, page_stride: int, slots, rows) -> None:
-    """Store each 352-byte row at its slot (in place). Slots equal to -1 are skipped."""
+    """Store each row (352-byte NVFP4 or 576-byte FP8) at its slot (in place). Slots equal to
+    -1 are skipped."""
     rows = np.asarray(rows, dtype=np.uint8)
+    row_bytes = rows.shape[1]
     for i, slot in enumerate(np.asarray(slots).tolist()):
         if slot < 0:
             continue
-        o = row_offset(slot, page_stride)
-        cache[o:o + ROW_BYTES] = rows[i]
+        o = row_offset(slot, page_stride, row_bytes)
+        cache[o:o + row_bytes] = rows[i]
 
 
 def logical_slot(block_table_row, position: int) -> int:
     """Physical slot of logical position ``position`` through one request's block table."""
-    return int(block_table_row[position // PAGE_ROWS]) * PAGE_ROWS + position % PAGE_ROWS
+    page = int(block_table_row[position // PAGE_ROWS])
+    if page < 0:
+        raise ValueError(f"logical_slot: position {position} falls in an unmapped page")
+    return page * PAGE_ROWS + position % PAGE_ROWS
 
 
-def read_rows(cache: np.ndarray, page_stride: int, block_table_row, positions) -> np.ndarray:
-    """Gather the 352-byte rows of the given logical positions of one request."""
+def read_rows(cache: np.ndarray, page_stride: int, block_table_row, positions,
+              row_bytes: int = ROW_BYTES) -> np.ndarray:
+    """Gather the rows (``row_bytes`` each) of the given logical positions of one request."""
     positions = np.asarray(positions).tolist()
-    out = np.empty((len(positions), ROW_BYTES), dtype=np.uint8)
+    out = np.empty((len(positions), row_bytes), dtype=np.uint8)
     for i, j in enumerate(positions):
-        o = row_offset(logical_slot(block_table_row, j), page_stride)
-        out[i] = cache[o:o + ROW_BYTES]
+        o = row_offset(logical_slot(block_table_row, j), page_stride, row_bytes)
+        out[i] = cache[o:o + row_bytes]
     return out
