@@ -64,6 +64,7 @@ typedef enum { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
 #define MLA_ROW_BYTES 352
 #define MLA_PAGE_ROWS 64
 #define MLA_MAX_TOPK 2048
+#define MLA_FP8_ROW_BYTES 576
 
 /* Quantize-on-append (page section "Making room for low-latency decode": the latent is stored
  * as NVFP4, the rope part as FP8).
@@ -129,6 +130,70 @@ mla_status mla_dense_decode(const void* q, mla_dtype q_dtype,
                             int32_t B, int32_t q_len, int32_t H, float softmax_scale,
                             int32_t split_tokens, int32_t num_splits, float* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- FP8 baseline and the staged path ------------------------------------------------------
+ * Page section "Making room for low-latency decode": before the NVFP4 change a row held the 512
+ * latent and the 64 rope values as FP8, 576 bytes. Section "Native NVFP4 sparse MLA decode
+ * kernel" compares the fused NVFP4 kernel with the FP8 kernel on such rows and with a staged path
+ * that first unpacks the selected NVFP4 rows into a temporary FP8 buffer, then runs the FP8
+ * kernel. FP8 row layout (576 bytes): latent element i at byte i, rope element j at byte 512+j,
+ * each the nearest E4M3 value (ties to even, saturated at 448, unit scale). Addressing as for the
+ * NVFP4 cache with 576 in place of 352; page_stride_bytes >= 64*576. */
+
+/* Append FP8 rows; arguments and behaviour as mla_nvfp4_quantize_append. */
+mla_status mla_fp8_append(const void* latent, int64_t latent_row_stride,
+                          const void* rope, int64_t rope_row_stride,
+                          const int64_t* slot_mapping, int64_t n_rows,
+                          void* kv_cache, int64_t page_stride_bytes,
+                          int64_t cache_bytes, hipStream_t stream);
+
+/* Sparse / dense decode over an FP8 cache: arguments, splits, workspace and results as
+ * mla_sparse_decode / mla_dense_decode (the same fused kernel with 576-byte rows converted to
+ * FP16 operands instead of 352-byte NVFP4 rows). */
+mla_status mla_fp8_sparse_decode(const void* q, mla_dtype q_dtype,
+                                 const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                                 const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* topk_idx, int32_t topk,
+                                 int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                                 int32_t num_splits, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+mla_status mla_fp8_dense_decode(const void* q, mla_dtype q_dtype,
+                                const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                                const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                                int32_t split_tokens, int32_t num_splits, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Staging pass of the staged path: for every query token tok = b*q_len + t and list entry e,
+ * the NVFP4 row topk_idx[tok][e] of request b is converted to a 576-byte FP8 row (each element's
+ * exact NVFP4 value rounded to E4M3, ties to even, saturated at 448; rope bytes copied) and
+ * written at staged_rows + (tok*P + e)*576, P = topk rounded up to a multiple of 64;
+ * staged_idx[tok][e] = e, or -1 for an empty entry (-1, or a position whose row is outside the
+ * table or the cache, as the decode kernels treat it); staged_block_table[tok][p] = tok*P/64 + p.
+ * The FP8 kernel then reads token tok as request tok of a cache with pages of 64*576 bytes.
+ *   staged_rows  B*q_len*P*576 bytes, 16-byte aligned (rows of empty entries are not written).
+ *   staged_idx   int32 [B*q_len, topk];  staged_block_table  int32 [B*q_len, P/64]. */
+mla_status mla_nvfp4_stage_fp8(const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                               const int32_t* block_table, int32_t max_pages,
+                               const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                               void* staged_rows, int32_t* staged_idx, int32_t* staged_block_table,
+                               hipStream_t stream);
+
+/* Workspace bytes of mla_staged_sparse_decode: staged rows, staged index list and block table,
+ * and the decode partials of `num_splits` splits, each part 256-byte aligned. */
+size_t mla_staged_workspace_size(int32_t num_tokens, int32_t H, int32_t topk, int32_t num_splits);
+
+/* The staged path: mla_nvfp4_stage_fp8 into the workspace, then mla_fp8_sparse_decode over the
+ * staged rows. Arguments as mla_sparse_decode over the NVFP4 cache; the workspace (always needed)
+ * comes from mla_staged_workspace_size. */
+mla_status mla_staged_sparse_decode(const void* q, mla_dtype q_dtype,
+                                    const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk,
+                                    int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                                    int32_t num_splits, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Test hook, off the hot path: decode the rows at `slots` (int64 [n]) into fp32 [n, 576]
  * (latent then rope), through the same on-chip decoder the attention kernels use. Values are

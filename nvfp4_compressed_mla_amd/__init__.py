@@ -10,6 +10,12 @@ from ._lib import (  # noqa: F401
     mla_decode_workspace_size,
     mla_dense_decode,
     mla_dense_decode_num_splits,
+    mla_fp8_append,
+    mla_fp8_dense_decode,
+    mla_fp8_sparse_decode,
+    mla_nvfp4_stage_fp8,
+    mla_staged_sparse_decode,
+    mla_staged_workspace_size,
     mla_nvfp4_dequantize_rows,
     mla_nvfp4_quantize_append,
     mla_set_timing_events,

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libmla_nvfp4.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_BF16, MLA_FP32 = 0, 1
 ROW_BYTES = 352
+FP8_ROW_BYTES = 576
 PAGE_ROWS = 64
 LATENT_DIM = 512
 QK_DIM = 576
@@ -28,6 +29,12 @@ EXPORTED = [
     "mla_sparse_decode",
     "mla_dense_decode",
     "mla_nvfp4_dequantize_rows",
+    "mla_fp8_append",
+    "mla_fp8_sparse_decode",
+    "mla_fp8_dense_decode",
+    "mla_nvfp4_stage_fp8",
+    "mla_staged_workspace_size",
+    "mla_staged_sparse_decode",
     "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
@@ -75,6 +82,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_dense_decode.restype = ctypes.c_int
     lib.mla_nvfp4_dequantize_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.mla_nvfp4_dequantize_rows.restype = ctypes.c_int
+    lib.mla_fp8_append.argtypes = lib.mla_nvfp4_quantize_append.argtypes
+    lib.mla_fp8_append.restype = ctypes.c_int
+    lib.mla_fp8_sparse_decode.argtypes = lib.mla_sparse_decode.argtypes
+    lib.mla_fp8_sparse_decode.restype = ctypes.c_int
+    lib.mla_fp8_dense_decode.argtypes = lib.mla_dense_decode.argtypes
+    lib.mla_fp8_dense_decode.restype = ctypes.c_int
+    lib.mla_nvfp4_stage_fp8.argtypes = [vp, i64, i64, vp, i32, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.mla_nvfp4_stage_fp8.restype = ctypes.c_int
+    lib.mla_staged_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.mla_staged_workspace_size.restype = sz
+    lib.mla_staged_sparse_decode.argtypes = lib.mla_sparse_decode.argtypes
+    lib.mla_staged_sparse_decode.restype = ctypes.c_int
     lib.mla_set_timing_events.argtypes = [vp, vp]
     lib.mla_set_timing_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -128,6 +147,16 @@ def _require(t, name, dtype=None, device=True):
 
 def mla_nvfp4_quantize_append(latent, rope, slot_mapping, kv_cache, page_stride_bytes, stream=None):
     """Quantize bf16 latent [N,512] / rope [N,64] rows into the cache at ``slot_mapping`` (int64)."""
+    _append("mla_nvfp4_quantize_append", latent, rope, slot_mapping, kv_cache, page_stride_bytes,
+            stream)
+
+
+def mla_fp8_append(latent, rope, slot_mapping, kv_cache, page_stride_bytes, stream=None):
+    """Write bf16 latent [N,512] / rope [N,64] rows as 576-byte FP8 rows at ``slot_mapping``."""
+    _append("mla_fp8_append", latent, rope, slot_mapping, kv_cache, page_stride_bytes, stream)
+
+
+def _append(name, latent, rope, slot_mapping, kv_cache, page_stride_bytes, stream):
     torch = _torch()
     _require(latent, "latent", torch.bfloat16)
     _require(rope, "rope", torch.bfloat16)
@@ -140,7 +169,7 @@ def mla_nvfp4_quantize_append(latent, rope, slot_mapping, kv_cache, page_stride_
     if not slot_mapping.is_contiguous() or slot_mapping.numel() != latent.shape[0]:
         raise ValueError("slot_mapping must be contiguous [N]")
     lib = load_library()
-    _check(lib.mla_nvfp4_quantize_append(
+    _check(getattr(lib, name)(
         _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(slot_mapping),
         latent.shape[0], _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(), _stream(stream)))
 
@@ -199,6 +228,33 @@ def mla_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, sof
     ``num_splits`` 0 picks the library's launch-shaping choice. ``workspace`` (uint8 device
     tensor) may be passed to keep the call free of allocations (graph capture).
     """
+    return _sparse("mla_sparse_decode", q, kv_cache, page_stride_bytes, block_table, topk_idx,
+                   softmax_scale, out, lse, num_splits, workspace, want_lse, stream)
+
+
+def mla_fp8_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,
+                          out=None, lse=None, num_splits: int = 0, workspace=None, want_lse=True,
+                          stream=None):
+    """Sparse decode over a cache of 576-byte FP8 rows; as :func:`mla_sparse_decode`."""
+    return _sparse("mla_fp8_sparse_decode", q, kv_cache, page_stride_bytes, block_table, topk_idx,
+                   softmax_scale, out, lse, num_splits, workspace, want_lse, stream)
+
+
+def mla_staged_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,
+                             out=None, lse=None, num_splits: int = 0, workspace=None,
+                             want_lse=True, stream=None):
+    """The staged path over an NVFP4 cache: selected rows converted to FP8 in the workspace,
+    then the FP8 kernel; arguments as :func:`mla_sparse_decode`."""
+    return _sparse("mla_staged_sparse_decode", q, kv_cache, page_stride_bytes, block_table,
+                   topk_idx, softmax_scale, out, lse, num_splits, workspace, want_lse, stream)
+
+
+def mla_staged_workspace_size(num_tokens: int, H: int, topk: int, num_splits: int) -> int:
+    return int(load_library().mla_staged_workspace_size(num_tokens, H, topk, num_splits))
+
+
+def _sparse(name, q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale, out, lse,
+            num_splits, workspace, want_lse, stream):
     torch = _torch()
     _require(q, "q")
     _require(kv_cache, "kv_cache", torch.uint8)
@@ -214,9 +270,15 @@ def mla_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, sof
     topk = topk_idx.shape[2]
     splits = num_splits or mla_sparse_decode_num_splits(B * q_len, H, topk, 0)
     out, lse = _outputs(q, out, lse, want_lse)
-    workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
+    if name == "mla_staged_sparse_decode":
+        need = mla_staged_workspace_size(B * q_len, H, topk, splits)
+        if workspace is None:
+            workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        ws_bytes = workspace.numel()
+    else:
+        workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
     lib = load_library()
-    _check(lib.mla_sparse_decode(
+    _check(getattr(lib, name)(
         _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
         _ptr(block_table), block_table.shape[1], _ptr(topk_idx), topk, B, q_len, H,
         float(softmax_scale), splits, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
@@ -228,6 +290,20 @@ def mla_dense_decode(q, kv_cache, page_stride_bytes, block_table, seq_lens, soft
                      split_tokens: int = 4096, out=None, lse=None, workspace=None, want_lse=True,
                      stream=None):
     """Dense decode over positions 0..seq_len-q_len+t; returns (out, lse)."""
+    return _dense("mla_dense_decode", q, kv_cache, page_stride_bytes, block_table, seq_lens,
+                  softmax_scale, split_tokens, out, lse, workspace, want_lse, stream)
+
+
+def mla_fp8_dense_decode(q, kv_cache, page_stride_bytes, block_table, seq_lens, softmax_scale,
+                         split_tokens: int = 4096, out=None, lse=None, workspace=None,
+                         want_lse=True, stream=None):
+    """Dense decode over a cache of 576-byte FP8 rows; as :func:`mla_dense_decode`."""
+    return _dense("mla_fp8_dense_decode", q, kv_cache, page_stride_bytes, block_table, seq_lens,
+                  softmax_scale, split_tokens, out, lse, workspace, want_lse, stream)
+
+
+def _dense(name, q, kv_cache, page_stride_bytes, block_table, seq_lens, softmax_scale,
+           split_tokens, out, lse, workspace, want_lse, stream):
     torch = _torch()
     _require(q, "q")
     _require(kv_cache, "kv_cache", torch.uint8)
@@ -244,7 +320,7 @@ def mla_dense_decode(q, kv_cache, page_stride_bytes, block_table, seq_lens, soft
     out, lse = _outputs(q, out, lse, want_lse)
     workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
     lib = load_library()
-    _check(lib.mla_dense_decode(
+    _check(getattr(lib, name)(
         _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, q_len, H,
         float(softmax_scale), int(split_tokens), splits, _ptr(out), _ptr(lse), _ptr(workspace),
@@ -263,6 +339,41 @@ def mla_nvfp4_dequantize_rows(kv_cache, page_stride_bytes, slots, stream=None):
     _check(lib.mla_nvfp4_dequantize_rows(_ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
                                          _ptr(slots), slots.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+def mla_nvfp4_stage_fp8(kv_cache, page_stride_bytes, block_table, topk_idx, staged_rows=None,
+                        staged_idx=None, staged_block_table=None, stream=None):
+    """Convert the selected NVFP4 rows to 576-byte FP8 rows (the staging pass of the staged path).
+
+    Returns (staged_rows uint8 [T*P*576], staged_idx int32 [T, topk], staged_block_table int32
+    [T, P/64]) with T = B*q_len and P = topk rounded up to a multiple of 64.
+    """
+    torch = _torch()
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 3 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous int32 [B, q_len, topk]")
+    B, q_len, topk = topk_idx.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    T, P = B * q_len, (topk + 63) // 64 * 64
+    dev = kv_cache.device
+    if staged_rows is None:
+        staged_rows = torch.empty(T * P * FP8_ROW_BYTES, device=dev, dtype=torch.uint8)
+    if staged_idx is None:
+        staged_idx = torch.empty(T, topk, device=dev, dtype=torch.int32)
+    if staged_block_table is None:
+        staged_block_table = torch.empty(T, P // 64, device=dev, dtype=torch.int32)
+    if staged_rows.numel() < T * P * FP8_ROW_BYTES or staged_idx.numel() != T * topk \
+            or staged_block_table.numel() != T * (P // 64):
+        raise ValueError("staged buffers have the wrong size")
+    lib = load_library()
+    _check(lib.mla_nvfp4_stage_fp8(
+        _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(), _ptr(block_table),
+        block_table.shape[1], _ptr(topk_idx), topk, B, q_len, _ptr(staged_rows), _ptr(staged_idx),
+        _ptr(staged_block_table), _stream(stream)))
+    return staged_rows, staged_idx, staged_block_table
 
 
 def mla_set_timing_events(start, stop) -> None:

@@ -36,14 +36,16 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kComputeUnits = 256;                 // MI355X: 8 XCDs x 32 CUs
 constexpr int64_t kMaxCacheBytes = int64_t(1) << 36;   // row offsets kept in 16-byte units (u32)
 
-mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_bytes) {
+mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_bytes,
+                       int64_t row_bytes = MLA_ROW_BYTES) {
   if (!kv_cache) return fail(MLA_ERR_INVALID_ARG, "kv_cache is null");
   if (!aligned(kv_cache, 16)) return fail(MLA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
-  if (page_stride < (int64_t)MLA_PAGE_ROWS * MLA_ROW_BYTES || page_stride % 16 != 0)
-    return fail(MLA_ERR_INVALID_ARG, "page_stride_bytes %lld must be >= 22528 and a multiple of 16",
-                (long long)page_stride);
-  if (cache_bytes < MLA_ROW_BYTES || cache_bytes > kMaxCacheBytes)
-    return fail(MLA_ERR_INVALID_ARG, "cache_bytes %lld out of range [352, 2^36]", (long long)cache_bytes);
+  if (page_stride < (int64_t)MLA_PAGE_ROWS * row_bytes || page_stride % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_stride_bytes %lld must be >= %lld and a multiple of 16",
+                (long long)page_stride, (long long)(MLA_PAGE_ROWS * row_bytes));
+  if (cache_bytes < row_bytes || cache_bytes > kMaxCacheBytes)
+    return fail(MLA_ERR_INVALID_ARG, "cache_bytes %lld out of range [%lld, 2^36]", (long long)cache_bytes,
+                (long long)row_bytes);
   return MLA_OK;
 }
 
@@ -61,10 +63,11 @@ mla_status check_decode_common(const void* q, mla_dtype q_dtype, const void* kv_
                                int64_t page_stride, int64_t cache_bytes,
                                const int32_t* block_table, int32_t max_pages, int32_t B,
                                int32_t q_len, int32_t H, float softmax_scale, int32_t num_splits,
-                               float* out, float* lse, void* workspace, size_t workspace_bytes) {
+                               float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               int64_t row_bytes = MLA_ROW_BYTES) {
   if (!q || !block_table || !out) return fail(MLA_ERR_INVALID_ARG, "null q / block_table / out");
   if (q_dtype != MLA_BF16 && q_dtype != MLA_FP32) return fail(MLA_ERR_UNSUPPORTED, "q_dtype must be bf16 or fp32");
-  mla_status st = check_cache(kv_cache, page_stride, cache_bytes);
+  mla_status st = check_cache(kv_cache, page_stride, cache_bytes, row_bytes);
   if (st != MLA_OK) return st;
   if (B < 1 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B and q_len must be >= 1");
   if (H < 16 || H % 16 != 0) return fail(MLA_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 16", H);
@@ -92,7 +95,7 @@ int32_t head_groups(int32_t H) {
   return nb / 4 + (nb % 4 != 0 ? 1 : 0);
 }
 
-mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, hipStream_t stream) {
+mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, bool fp8, hipStream_t stream) {
   const int64_t T = (int64_t)a.B * a.q_len;
   const int32_t S = a.n_split;
   const int32_t T32 = (int32_t)T;
@@ -111,7 +114,7 @@ mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, hipStream_t stre
     a.n_hg = groups;
     a.total_items = T32 * groups * S;
     a.items_per_xcd = (a.total_items + 7) / 8;
-    hipError_t e = mla::launch_decode(a, nh, dense, stream);
+    hipError_t e = mla::launch_decode(a, nh, dense, fp8, stream);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");
   }
   if (g_timing_stop) {
@@ -197,16 +200,21 @@ int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens) {
   return (int32_t)((n + split_tokens - 1) / split_tokens);
 }
 
-mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
-                             int64_t page_stride_bytes, int64_t cache_bytes,
-                             const int32_t* block_table, int32_t max_pages,
-                             const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
-                             int32_t H, float softmax_scale, int32_t num_splits, float* out,
-                             float* lse, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status sparse_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const void* kv_cache,
+                              int64_t page_stride_bytes, int64_t cache_bytes,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                              int32_t H, float softmax_scale, int32_t num_splits, float* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
                                       block_table, max_pages, B, q_len, H, softmax_scale,
-                                      num_splits, out, lse, workspace, workspace_bytes);
+                                      num_splits, out, lse, workspace, workspace_bytes,
+                                      fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
   if (st != MLA_OK) return st;
   if (!topk_idx) return fail(MLA_ERR_INVALID_ARG, "topk_idx is null");
   if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
@@ -236,18 +244,20 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_ca
     a.ws_o = (_Float16*)workspace;
     a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
   }
-  return run_decode(a, H, false, stream);
+  return run_decode(a, H, false, fp8, stream);
 }
 
-mla_status mla_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
-                            int64_t page_stride_bytes, int64_t cache_bytes,
-                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                            int32_t B, int32_t q_len, int32_t H, float softmax_scale,
-                            int32_t split_tokens, int32_t num_splits, float* out, float* lse,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+mla_status dense_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const void* kv_cache,
+                             int64_t page_stride_bytes, int64_t cache_bytes,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H,
+                             float softmax_scale, int32_t split_tokens, int32_t num_splits,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
                                       block_table, max_pages, B, q_len, H, softmax_scale,
-                                      num_splits, out, lse, workspace, workspace_bytes);
+                                      num_splits, out, lse, workspace, workspace_bytes,
+                                      fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
   if (st != MLA_OK) return st;
   if (!seq_lens) return fail(MLA_ERR_INVALID_ARG, "seq_lens is null");
   if (split_tokens < 64 || split_tokens % 64 != 0 || split_tokens > mla::kMaxDensePages * MLA_PAGE_ROWS)
@@ -277,7 +287,158 @@ mla_status mla_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cac
     a.ws_o = (_Float16*)workspace;
     a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
   }
-  return run_decode(a, H, true, stream);
+  return run_decode(a, H, true, fp8, stream);
+}
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Staged-path workspace: FP8 rows, staged index list, staged block table, decode partials.
+struct StagedLayout {
+  size_t rows, idx, bt, dec, total;
+};
+
+StagedLayout staged_layout(int64_t T, int32_t H, int32_t topk, int32_t num_splits) {
+  const int64_t topk_pad = (topk + 63) & ~63;
+  StagedLayout l;
+  l.rows = 0;
+  l.idx = round256((size_t)(T * topk_pad * MLA_FP8_ROW_BYTES));
+  l.bt = l.idx + round256((size_t)(T * topk) * 4);
+  l.dec = l.bt + round256((size_t)(T * (topk_pad / 64)) * 4);
+  l.total = l.dec + ws_bytes(T, H, num_splits);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                             int64_t page_stride_bytes, int64_t cache_bytes,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                             int32_t H, float softmax_scale, int32_t num_splits, float* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return sparse_decode_impl(false, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                            block_table, max_pages, topk_idx, topk, B, q_len, H, softmax_scale,
+                            num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_fp8_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                 int64_t page_stride_bytes, int64_t cache_bytes,
+                                 const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                                 int32_t H, float softmax_scale, int32_t num_splits, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return sparse_decode_impl(true, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                            block_table, max_pages, topk_idx, topk, B, q_len, H, softmax_scale,
+                            num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                            int64_t page_stride_bytes, int64_t cache_bytes,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                            int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                            int32_t split_tokens, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dense_decode_impl(false, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                           block_table, max_pages, seq_lens, B, q_len, H, softmax_scale,
+                           split_tokens, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_fp8_dense_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                int64_t page_stride_bytes, int64_t cache_bytes,
+                                const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H,
+                                float softmax_scale, int32_t split_tokens, int32_t num_splits,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return dense_decode_impl(true, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                           block_table, max_pages, seq_lens, B, q_len, H, softmax_scale,
+                           split_tokens, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_fp8_append(const void* latent, int64_t latent_row_stride, const void* rope,
+                          int64_t rope_row_stride, const int64_t* slot_mapping, int64_t n_rows,
+                          void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                          hipStream_t stream) {
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  mla_status st = check_cache(kv_cache, page_stride_bytes, cache_bytes, MLA_FP8_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (n_rows == 0) return hip_status(hipSuccess, "");
+  if (!latent || !rope || !slot_mapping) return fail(MLA_ERR_INVALID_ARG, "null latent / rope / slot_mapping");
+  if (!aligned(latent, 16) || latent_row_stride < MLA_LATENT_DIM || latent_row_stride % 8 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "latent must be 16-byte aligned with a row stride >= 512 and a multiple of 8");
+  if (!aligned(rope, 2) || rope_row_stride < MLA_ROPE_DIM)
+    return fail(MLA_ERR_INVALID_ARG, "rope must be 2-byte aligned with a row stride >= 64");
+  if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  return hip_status(mla::launch_fp8_append(latent, latent_row_stride, rope, rope_row_stride,
+                                           slot_mapping, n_rows, kv_cache, page_stride_bytes,
+                                           cache_bytes, stream),
+                    "fp8_append launch");
+}
+
+mla_status mla_nvfp4_stage_fp8(const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                               const int32_t* block_table, int32_t max_pages,
+                               const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                               void* staged_rows, int32_t* staged_idx, int32_t* staged_block_table,
+                               hipStream_t stream) {
+  mla_status st = check_cache(kv_cache, page_stride_bytes, cache_bytes);
+  if (st != MLA_OK) return st;
+  if (!block_table || !topk_idx || !staged_rows || !staged_idx || !staged_block_table)
+    return fail(MLA_ERR_INVALID_ARG, "null block_table / topk_idx / staged buffers");
+  if (B < 1 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B and q_len must be >= 1");
+  if (max_pages < 1 || (int64_t)max_pages * MLA_PAGE_ROWS > (int64_t)1 << 30)
+    return fail(MLA_ERR_INVALID_ARG, "max_pages out of range");
+  if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
+  if (!aligned(staged_rows, 16) || !aligned(staged_idx, 4) || !aligned(staged_block_table, 4) ||
+      !aligned(topk_idx, 4) || !aligned(block_table, 4))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned staged buffers or index arrays");
+  const int64_t T = (int64_t)B * q_len;
+  if (T > (int64_t)1 << 20) return fail(MLA_ERR_INVALID_ARG, "too many query tokens");
+  return hip_status(mla::launch_stage_fp8(kv_cache, page_stride_bytes, cache_bytes, block_table,
+                                          max_pages, topk_idx, topk, (int32_t)T, q_len, staged_rows,
+                                          staged_idx, staged_block_table, stream),
+                    "stage_fp8 launch");
+}
+
+size_t mla_staged_workspace_size(int32_t num_tokens, int32_t H, int32_t topk, int32_t num_splits) {
+  if (num_tokens < 1 || H < 1 || topk < 1) return 0;
+  return staged_layout(num_tokens, H, topk, num_splits).total;
+}
+
+mla_status mla_staged_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk, int32_t B,
+                                    int32_t q_len, int32_t H, float softmax_scale,
+                                    int32_t num_splits, float* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                                      block_table, max_pages, B, q_len, H, softmax_scale,
+                                      num_splits, out, lse, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!topk_idx) return fail(MLA_ERR_INVALID_ARG, "topk_idx is null");
+  if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
+  const int64_t T = (int64_t)B * q_len;
+  const int64_t staged_bytes = T * ((topk + 63) & ~63) * MLA_FP8_ROW_BYTES;
+  if (staged_bytes > kMaxCacheBytes) return fail(MLA_ERR_INVALID_ARG, "staged rows exceed 2^36 bytes");
+  const StagedLayout l = staged_layout(T, H, topk, num_splits);
+  if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_WORKSPACE, "the staged path needs a 256-byte aligned workspace");
+  if (workspace_bytes < l.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, l.total);
+  uint8_t* ws = (uint8_t*)workspace;
+  const int32_t topk_pad = (topk + 63) & ~63;
+  st = mla_nvfp4_stage_fp8(kv_cache, page_stride_bytes, cache_bytes, block_table, max_pages,
+                           topk_idx, topk, B, q_len, ws + l.rows, (int32_t*)(ws + l.idx),
+                           (int32_t*)(ws + l.bt), stream);
+  if (st != MLA_OK) return st;
+  // every query token is its own "request" over its staged rows
+  return sparse_decode_impl(true, q, q_dtype, ws + l.rows, (int64_t)MLA_PAGE_ROWS * MLA_FP8_ROW_BYTES,
+                            (int64_t)T * topk_pad * MLA_FP8_ROW_BYTES, (const int32_t*)(ws + l.bt),
+                            topk_pad / 64, (const int32_t*)(ws + l.idx), topk, (int32_t)T, 1, H,
+                            softmax_scale, num_splits, out, lse, ws + l.dec, l.total - l.dec, stream);
 }
 
 mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,

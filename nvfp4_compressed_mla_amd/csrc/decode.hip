@@ -58,7 +58,7 @@ constexpr int kThreads = 768;
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 
 // Source of every load that has no row behind it (padding rows, padding pieces, bad pages).
-__device__ __attribute__((aligned(16))) uint8_t g_zero_row[512] = {0};
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[kFp8RowBytes] = {0};
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
@@ -140,9 +140,13 @@ __device__ __forceinline__ half4v lds_tr16(const uint8_t* p) {
 constexpr int kDecSlots = 3;
 constexpr int kProducers = 8;                                 // producer waves (2 per SIMD)
 
-template <int NH, bool DENSE>
+// FP8 selects 576-byte FP8 rows (the baseline format): they need no group scales, so the
+// producer waves load their bytes straight into registers two tiles ahead and convert them,
+// and the math waves issue no gathers.
+template <int NH, bool DENSE, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTileBytes];
+  constexpr int RB = FP8 ? kFp8RowBytes : kRowBytes;     // bytes per cache row
+  __shared__ __attribute__((aligned(16))) uint8_t raw[FP8 ? 1 : kRawSlots][FP8 ? 16 : kRawTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t dec[kDecSlots][kDecTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][NH * 16 * kPStride];
   __shared__ __attribute__((aligned(16))) float alpha_s[2][NH * 16];
@@ -233,8 +237,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         bool ok = false;
         uint32_t o16 = 0;
         if (pg[r] >= 0) {
-          const int64_t off = (int64_t)pg[r] * a.page_stride + (int64_t)(jv[r] & 63) * kRowBytes;
-          if (off + kRowBytes <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
+          const int64_t off = (int64_t)pg[r] * a.page_stride + (int64_t)(jv[r] & 63) * RB;
+          if (off + RB <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
         }
         const uint64_t mask = __ballot(ok);
         if (lane == 0) cnt_s[r][pw] = __popcll(mask);
@@ -311,8 +315,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       } else {
         const int pos = p0 + (ok ? row : 0);
         const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-        const uint32_t o = pb + (uint32_t)(pos & 63) * (kRowBytes / 16);
-        o16[k] = (ok && pb != kInvalid && (int64_t)o * 16 + kRowBytes <= a.cache_bytes) ? o : kInvalid;
+        const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
+        o16[k] = (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
       }
     }
   };
@@ -341,18 +345,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // loads would otherwise also wait for the gathers, which share the vector-memory counter.
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) asm volatile("" : "+v"(qf[c]));
-    {
+    if constexpr (!FP8) {
       uint32_t o16[3];
       tile_offsets(0, o16); issue_tile(0, o16);
       tile_offsets(1, o16); issue_tile(1, o16);
       tile_offsets(2, o16); issue_tile(2, o16);
     }
-    wait_tiles(2);
+    if constexpr (!FP8) wait_tiles(2);
     lds_barrier();                            // prologue: tile 0 in LDS
-    wait_tiles(1);
+    if constexpr (!FP8) wait_tiles(1);
     lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
-    uint32_t next_o16[3];                     // row offsets of the next tile to gather
-    tile_offsets(3, next_o16);
+    uint32_t next_o16[3] = {kInvalid, kInvalid, kInvalid};   // row offsets of the next tile to gather
+    if constexpr (!FP8) tile_offsets(3, next_o16);
     float m_run = -INFINITY, l_run = 0.0f;     // running max (log2 units), partial sum
     const int kslot = ((kg << 4) + (l16 ^ ((kg & 1) << 2))) << 4;   // QK A-fragment slot
     for (int i = 0; i <= n_tiles; ++i) {
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         uint32_t cur_o16[3] = {next_o16[0], next_o16[1], next_o16[2]};
-        tile_offsets(i + 4, next_o16);                // their LDS latency hides behind the softmax
+        if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
         float sv[8];
         float mx = -INFINITY;
 #pragma unroll
@@ -413,10 +417,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         const uint64_t any = __ballot(move && i > 0);
         if (lane == 0) flag_s[i & 1][w] = any != 0ull;
         if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
-        issue_tile(i + 3, cur_o16);
+        if constexpr (!FP8) issue_tile(i + 3, cur_o16);
       }
-      if (!(qk_wave && i < n_tiles)) { issue_tile(i + 3, next_o16); tile_offsets(i + 4, next_o16); }
-      wait_tiles(1);
+      if constexpr (!FP8) {
+        if (!(qk_wave && i < n_tiles)) { issue_tile(i + 3, next_o16); tile_offsets(i + 4, next_o16); }
+        wait_tiles(1);
+      }
       lds_barrier();
     }
     wait_vmcnt<0>();                          // no gather may still target LDS at exit
@@ -454,14 +460,58 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     };
     auto decode_tile = [&](int tile) { decode_store(tile, decode_load(tile)); };
 
+    // FP8 rows: lane (pw, kg, l16) loads bytes 32*dp..32*dp+31 of row drow (K-chunk dp) and rope
+    // bytes 4*rq..4*rq+3 of row ptid & 31 (rq = ptid >> 5), straight into registers.
+    const int rq = ptid >> 5, rqrow = ptid & 31;
+    struct Fp8In { uint4v a, b; uint32_t r; };
+    auto row_src = [&](int row) -> const uint8_t* {
+      uint32_t o16;
+      if constexpr (!DENSE) {
+        o16 = row < n_rows ? rowoff[row] : kInvalid;
+      } else {
+        const bool ok = row < n_rows;
+        const int pos = p0 + (ok ? row : 0);
+        const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
+        const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
+        o16 = (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
+      }
+      return o16 != kInvalid ? a.cache + (int64_t)o16 * 16 : g_zero_row;
+    };
+    auto fp8_load = [&](int tile) {
+      Fp8In d;
+      const uint8_t* p = row_src(tile * kTileRows + drow) + 32 * dp;
+      d.a = *(const uint4v*)p;
+      d.b = *(const uint4v*)(p + 16);
+      d.r = *(const uint32_t*)(row_src(tile * kTileRows + rqrow) + kLatent + 4 * rq);
+      return d;
+    };
+    auto fp8_store = [&](int tile, const Fp8In& d) {
+      uint8_t* dst = dec[tile % kDecSlots];
+      *(half8v*)(dst + frag_off(drow, dp, 0)) = decode_fp8x8(d.a[0], d.a[1]);
+      *(half8v*)(dst + frag_off(drow, dp, 1)) = decode_fp8x8(d.a[2], d.a[3]);
+      *(half8v*)(dst + frag_off(drow, dp, 2)) = decode_fp8x8(d.b[0], d.b[1]);
+      *(half8v*)(dst + frag_off(drow, dp, 3)) = decode_fp8x8(d.b[2], d.b[3]);
+      const half2v r0 = fp8x2_to_half2<false>(d.r), r1 = fp8x2_to_half2<true>(d.r);
+      *(half4v*)(dst + frag_off(rqrow, 16 + (rq >> 3), (rq >> 1) & 3) + 8 * (rq & 1)) =
+          half4v{r0[0], r0[1], r1[0], r1[1]};
+    };
+
     // Output accumulators of dims 64*pw + 16*n + l16, heads 16*hb + 4*kg + e.
     float4v o[NH][4];
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb)
 #pragma unroll
       for (int n = 0; n < 4; ++n) o[hb][n] = float4v{0.f, 0.f, 0.f, 0.f};
-    lds_barrier();                            // prologue: tile 0 in LDS
-    if (n_tiles > 0) decode_tile(0);
+    Fp8In f1{};                               // FP8: registers of the next tile to convert
+    if constexpr (FP8) {
+      const Fp8In f0 = fp8_load(0);
+      f1 = fp8_load(1);
+      lds_barrier();                          // prologue (same barrier count as the gathers)
+      if (n_tiles > 0) fp8_store(0, f0);
+    } else {
+      lds_barrier();                          // prologue: tile 0 in LDS
+      if (n_tiles > 0) decode_tile(0);
+    }
     lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
     // Transposing-read offsets (V operand of PV): the lane supplies 4 dims
     // (16*n + 4*(l16&3) ..) of row 8*kg + (l16>>2) (+4 for the second read).
@@ -471,7 +521,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // raw bytes of tile i+1 first: their LDS latency hides behind PV(i-1)
       const bool dec_next = i + 1 < n_tiles;
       DecodeIn din;
-      if (dec_next) din = decode_load(i + 1);
+      Fp8In f2;
+      if constexpr (FP8) f2 = fp8_load(i + 2);         // lands while PV(i-1) runs
+      else if (dec_next) din = decode_load(i + 1);
       if (i >= 1) {
         // PV(i-1): rescale by alpha(i-1) where the running max moved, then O += P V.
         const int j = i - 1;
@@ -505,7 +557,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int hb = 0; hb < NH; ++hb) o[hb][n] = mfma16(pa[hb], vb, o[hb][n]);
         }
       }
-      if (dec_next) decode_store(i + 1, din);
+      if constexpr (FP8) {
+        if (dec_next) fp8_store(i + 1, f1);
+        f1 = f2;
+      } else if (dec_next) {
+        decode_store(i + 1, din);
+      }
       lds_barrier();
     }
     lds_barrier();                              // fin_m / fin_l written by the math waves
@@ -625,21 +682,28 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream) {
   const dim3 grid((unsigned)a.items_per_xcd * 8), block(kThreads);
-#define MLA_LAUNCH(NHV, DV) \
-  hipLaunchKernelGGL((decode_kernel<NHV, DV>), grid, block, 0, stream, a)
-  switch (nh * 2 + (dense ? 1 : 0)) {
-    case 2: MLA_LAUNCH(1, false); break;
-    case 3: MLA_LAUNCH(1, true); break;
-    case 4: MLA_LAUNCH(2, false); break;
-    case 5: MLA_LAUNCH(2, true); break;
-    case 6: MLA_LAUNCH(3, false); break;
-    case 7: MLA_LAUNCH(3, true); break;
-    case 8: MLA_LAUNCH(4, false); break;
-    case 9: MLA_LAUNCH(4, true); break;
-    default: return hipErrorInvalidValue;
+#define MLA_LAUNCH(NHV, DV, FV) \
+  hipLaunchKernelGGL((decode_kernel<NHV, DV, FV>), grid, block, 0, stream, a)
+#define MLA_CASES(FV)                           \
+  switch (nh * 2 + (dense ? 1 : 0)) {           \
+    case 2: MLA_LAUNCH(1, false, FV); break;    \
+    case 3: MLA_LAUNCH(1, true, FV); break;     \
+    case 4: MLA_LAUNCH(2, false, FV); break;    \
+    case 5: MLA_LAUNCH(2, true, FV); break;     \
+    case 6: MLA_LAUNCH(3, false, FV); break;    \
+    case 7: MLA_LAUNCH(3, true, FV); break;     \
+    case 8: MLA_LAUNCH(4, false, FV); break;    \
+    case 9: MLA_LAUNCH(4, true, FV); break;     \
+    default: return hipErrorInvalidValue;       \
   }
+  if (fp8) {
+    MLA_CASES(true)
+  } else {
+    MLA_CASES(false)
+  }
+#undef MLA_CASES
 #undef MLA_LAUNCH
   return hipGetLastError();
 }

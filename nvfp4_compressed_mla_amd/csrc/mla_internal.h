@@ -43,8 +43,20 @@ hipError_t launch_quantize_append(const void* latent, int64_t latent_stride, con
 hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_t cache_bytes,
                                   const int64_t* slots, int64_t n, float* out, hipStream_t stream);
 
-// nh = heads per workgroup / 16 (1..4); dense selects implicit positions.
-hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, hipStream_t stream);
+// nh = heads per workgroup / 16 (1..4); dense selects implicit positions; fp8 selects 576-byte
+// FP8 rows instead of 352-byte NVFP4 rows.
+hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream);
+
+hipError_t launch_fp8_append(const void* latent, int64_t latent_stride, const void* rope,
+                             int64_t rope_stride, const int64_t* slots, int64_t n_rows, void* cache,
+                             int64_t page_stride, int64_t cache_bytes, hipStream_t stream);
+
+// Staged NVFP4 -> FP8 rows of the selected entries: staged [T, ceil64(topk), 576] bytes,
+// staged_idx int32 [T, topk], staged_bt int32 [T, ceil64(topk)/64].
+hipError_t launch_stage_fp8(const void* cache, int64_t page_stride, int64_t cache_bytes,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* topk_idx,
+                            int32_t topk, int32_t T, int32_t q_len, void* staged,
+                            int32_t* staged_idx, int32_t* staged_bt, hipStream_t stream);
 
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream);

@@ -36,6 +36,9 @@ constexpr int kCodeBytes = 256;   // 512 4-bit codes
 constexpr int kScaleOff = 256;    // 32 E4M3 group scales
 constexpr int kRopeOff = 288;     // 64 E4M3 rope values
 constexpr int kPageRows = 64;
+// FP8 baseline row (576 bytes): latent element i at byte i, rope element j at byte 512 + j, both
+// E4M3 with unit scale.
+constexpr int kFp8RowBytes = 576;
 
 // ---- encode --------------------------------------------------------------------------------
 

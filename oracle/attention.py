@@ -96,8 +96,10 @@ def dense_positions(seq_len: int, q_len: int, t: int):
     return list(range(0, max(0, last + 1)))
 
 
-def dense_decode(q, cache, page_stride, block_table, seq_lens, softmax_scale, tokens=None):
-    """Dense decode: query token t of request b attends to positions 0..seq_len-q_len+t."""
+def dense_decode(q, cache, page_stride, block_table, seq_lens, softmax_scale, tokens=None,
+                 row_bytes=ROW_BYTES):
+    """Dense decode: query token t of request b attends to positions 0..seq_len-q_len+t.
+    ``row_bytes``: 352 for the NVFP4 cache, 576 for the FP8 baseline cache."""
     q = np.asarray(q, dtype=np.float64)
     b_n, q_len, h, _ = q.shape
     out = np.full((b_n, q_len, h, LATENT_DIM), np.nan)
@@ -105,7 +107,7 @@ def dense_decode(q, cache, page_stride, block_table, seq_lens, softmax_scale, to
     todo = tokens if tokens is not None else [(b, t) for b in range(b_n) for t in range(q_len)]
     for b, t in todo:
         pos = dense_positions(int(seq_lens[b]), q_len, t)
-        rows = read_rows(cache, page_stride, block_table[b], pos)
+        rows = read_rows(cache, page_stride, block_table[b], pos, row_bytes)
         keys, values = rows_to_kv(rows)
         out[b, t], lse[b, t] = attend(q[b, t], keys, values, softmax_scale)
     return out, lse

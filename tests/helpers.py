@@ -15,9 +15,11 @@ import torch
 from nvfp4_compressed_mla_amd import workloads as wl
 from oracle import attention as oa
 from oracle import cache as oc
+from oracle import fp8 as f8
 from oracle import nvfp4 as nv
 
 PAGE_BYTES = 64 * 352
+FP8_PAGE_BYTES = 64 * 576
 ROW_TOL = 2e-3          # max over a row of |out - ref| / max |ref|, the stated parity bar
 LSE_TOL = 2e-3          # absolute, natural log
 
@@ -39,21 +41,29 @@ class Case:
     q: torch.Tensor             # [B, q_len, H, 576]
     topk_idx: torch.Tensor      # int32 [B, q_len, topk] (None for dense)
     seq_lens: torch.Tensor      # int32 [B]
+    fmt: str = "nvfp4"          # "nvfp4" (352-byte rows) or "fp8" (576-byte rows)
+
+    @property
+    def row_bytes(self) -> int:
+        return 576 if self.fmt == "fp8" else 352
 
 
 def softmax_scale() -> float:
     return 1.0 / math.sqrt(576.0)
 
 
-def build_case(B, q_len, H, ctx, topk, seed, q_dtype="bf16", page_stride=PAGE_BYTES,
-               device="cuda", spare_pages=3, topk_fn=None, append_rows=0):
+def build_case(B, q_len, H, ctx, topk, seed, q_dtype="bf16", page_stride=None,
+               device="cuda", spare_pages=3, topk_fn=None, append_rows=0, fmt="nvfp4"):
     """Generate inputs on the device and quantize them into a paged cache with the HIP path.
 
     ``append_rows`` > 0 writes the last ``append_rows`` positions of every request with a second
     quantize-append call covering all requests at once (a serving step's append), after the
-    history rows.
+    history rows. ``fmt`` "fp8" writes 576-byte FP8 rows instead of NVFP4 rows.
     """
-    from nvfp4_compressed_mla_amd import mla_nvfp4_quantize_append
+    import nvfp4_compressed_mla_amd as m
+    if page_stride is None:
+        page_stride = FP8_PAGE_BYTES if fmt == "fp8" else PAGE_BYTES
+    mla_nvfp4_quantize_append = m.mla_fp8_append if fmt == "fp8" else m.mla_nvfp4_quantize_append
     ctx = list(ctx)
     total = sum(ctx)
     latent, rope = wl.gen_latent_rope(total, seed, device)
@@ -83,7 +93,7 @@ def build_case(B, q_len, H, ctx, topk, seed, q_dtype="bf16", page_stride=PAGE_BY
         idx = (topk_fn or wl.gen_topk)(B, q_len, topk, ctx, seed + 3, device)
     seq = torch.tensor(ctx, dtype=torch.int32, device=device)
     return Case(B, q_len, H, ctx, topk, page_stride, latent, rope, row_base, bt, n_pages, cache,
-                q, idx, seq)
+                q, idx, seq, fmt)
 
 
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
@@ -107,7 +117,7 @@ def oracle_cache(case: Case, positions_per_request=None) -> np.ndarray:
                 continue
         rows_lat = bf16_to_f64(case.latent[case.row_base[b] + torch.as_tensor(pos, device=case.latent.device)])
         rows_rope = bf16_to_f64(case.rope[case.row_base[b] + torch.as_tensor(pos, device=case.rope.device)])
-        enc = nv.quantize_rows(rows_lat, rows_rope)
+        enc = (f8.quantize_rows_fp8 if case.fmt == "fp8" else nv.quantize_rows)(rows_lat, rows_rope)
         slots = [oc.logical_slot(bt[b], int(j)) for j in pos]
         oc.write_rows(cache, case.page_stride, slots, enc)
     return cache
@@ -118,7 +128,8 @@ def oracle_sparse(case: Case, tokens=None, cache=None):
         cache = oracle_cache(case)
     q = case.q.detach().float().cpu().numpy().astype(np.float64)
     return oa.sparse_decode(q, cache, case.page_stride, case.block_table.cpu().numpy(),
-                            case.topk_idx.cpu().numpy(), softmax_scale(), tokens=tokens)
+                            case.topk_idx.cpu().numpy(), softmax_scale(), tokens=tokens,
+                            row_bytes=case.row_bytes)
 
 
 def oracle_dense(case: Case, tokens=None, cache=None):
@@ -126,7 +137,21 @@ def oracle_dense(case: Case, tokens=None, cache=None):
         cache = oracle_cache(case)
     q = case.q.detach().float().cpu().numpy().astype(np.float64)
     return oa.dense_decode(q, cache, case.page_stride, case.block_table.cpu().numpy(),
-                           case.seq_lens.cpu().numpy(), softmax_scale(), tokens=tokens)
+                           case.seq_lens.cpu().numpy(), softmax_scale(), tokens=tokens,
+                           row_bytes=case.row_bytes)
+
+
+def oracle_staged_cache(case: Case, cache=None) -> np.ndarray:
+    """The staged path's FP8 rows, by the oracle: each row of the oracle's NVFP4 cache converted
+    to a 576-byte FP8 row at the same slot of a cache with 64*576-byte pages."""
+    if cache is None:
+        cache = oracle_cache(case)
+    n_slots = case.n_pages * 64
+    out = np.zeros(case.n_pages * FP8_PAGE_BYTES, dtype=np.uint8)
+    rows = np.stack([cache[oc.row_offset(s, case.page_stride):oc.row_offset(s, case.page_stride) + 352]
+                     for s in range(n_slots)])
+    oc.write_rows(out, FP8_PAGE_BYTES, np.arange(n_slots), f8.nvfp4_rows_to_fp8(rows))
+    return out
 
 
 def assert_parity(out, lse, ref_out, ref_lse, tokens=None, what=""):

@@ -130,3 +130,39 @@ def test_launch_shaping(lib):
     assert lib.mla_decode_workspace_size(32, 64, 1) == 0
     assert lib.mla_decode_workspace_size(32, 64, 8) == 32 * 8 * 64 * (512 * 2 + 4)
     assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
+
+
+def test_fp8_entry_points_reject(lib):
+    f = lib.mla_fp8_append
+    assert f(FAKE, 512, FAKE, 64, FAKE, 0, FAKE, 36864, 36864, None) == OK
+    assert f(FAKE, 512, FAKE, 64, FAKE, 5, FAKE, 22528, 36864, None) == INVALID   # page < 64*576
+    assert f(FAKE, 512, FAKE, 64, FAKE, 5, FAKE, 36864, 500, None) == INVALID     # < one row
+    d = lib.mla_fp8_sparse_decode
+    args = [FAKE, 0, FAKE, 36864, 36864 * 4, FAKE, 4, FAKE, 256, 1, 1, 16, 0.04, 1, FAKE, None,
+            None, 0, None]
+    bad = list(args)
+    bad[3] = 22528                                   # an NVFP4 page stride is too small here
+    assert d(*bad) == INVALID
+    bad = list(args)
+    bad[8] = 4096
+    assert d(*bad) == UNSUPPORTED
+    s = lib.mla_staged_sparse_decode
+    nv = [FAKE, 0, FAKE, 22528, 22528 * 4, FAKE, 4, FAKE, 256, 1, 1, 16, 0.04, 1, FAKE, None,
+          None, 0, None]
+    assert s(*nv) == WORKSPACE                       # the staged path always needs a workspace
+    nv[16], nv[17] = FAKE, 100
+    assert s(*nv) == WORKSPACE
+    g = lib.mla_nvfp4_stage_fp8
+    assert g(FAKE, 22528, 22528 * 4, FAKE, 4, FAKE, 256, 1, 1, None, FAKE, FAKE, None) == INVALID
+    assert g(FAKE, 22528, 22528 * 4, FAKE, 4, FAKE, 0, 1, 1, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_staged_workspace_size(lib):
+    T, H, k = 15, 16, 2048
+    rows = T * k * 576
+    idx = T * k * 4
+    bt = (T * (k // 64) * 4 + 255) // 256 * 256
+    assert lib.mla_staged_workspace_size(T, H, k, 1) == rows + idx + bt
+    assert lib.mla_staged_workspace_size(T, H, k, 4) == rows + idx + bt + T * 4 * H * (512 * 2 + 4)
+    # topk padded to whole 64-row pages
+    assert lib.mla_staged_workspace_size(1, 16, 100, 1) == 128 * 576 + 512 + 256
