@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PAGE = 64 * 352
+FP8_PAGE = 64 * 576
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batched_counters.txt")
@@ -56,14 +57,23 @@ def kernel_source_hash() -> str:
 # ---- workload construction ---------------------------------------------------------------------
 
 class SparseWorkload:
-    """Caches, tables, rotated queries / index lists and preallocated outputs of one config."""
+    """Caches, tables, rotated queries / index lists and preallocated outputs of one config.
+
+    ``fmt``: "nvfp4" (the fused NVFP4 kernel), "fp8" (the same inputs as 576-byte FP8 rows, the
+    fused FP8 kernel) or "staged" (NVFP4 cache; selected rows converted to FP8 in a workspace,
+    then the FP8 kernel).
+    """
 
     def __init__(self, name, B, q_len, H, ctx, topk, append_rows, rotations, seed, device,
-                 q_lens=None, keep_latent=False):
+                 q_lens=None, keep_latent=False, fmt="nvfp4"):
         import torch
         from nvfp4_compressed_mla_amd import workloads as wl
         import nvfp4_compressed_mla_amd as m
         self.name, self.B, self.q_len, self.H, self.topk = name, B, q_len, H, topk
+        self.fmt = fmt
+        self.page = FP8_PAGE if fmt == "fp8" else PAGE
+        self.row_bytes = 576 if fmt == "fp8" else 352
+        append_fn = m.mla_fp8_append if fmt == "fp8" else m.mla_nvfp4_quantize_append
         self.ctx = list(ctx)
         self.append_rows = append_rows
         self.q_lens = q_lens
@@ -72,10 +82,10 @@ class SparseWorkload:
         # pages for the existing rows plus the rows this step appends
         bt, n_pages = wl.gen_block_table(self.ctx, seed + 1, device)
         self.block_table = bt
-        self.cache = torch.zeros(n_pages * PAGE, dtype=torch.uint8, device=device)
+        self.cache = torch.zeros(n_pages * self.page, dtype=torch.uint8, device=device)
         lat, rope = wl.gen_latent_rope(total_rows, seed, device)
         slots = torch.cat([wl.slot_mapping_for(bt, b, 0, c) for b, c in enumerate(existing)])
-        m.mla_nvfp4_quantize_append(lat, rope, slots, self.cache, PAGE)
+        append_fn(lat, rope, slots, self.cache, self.page)
         self.row_base = [0]
         for c in existing[:-1]:
             self.row_base.append(self.row_base[-1] + c)
@@ -96,6 +106,8 @@ class SparseWorkload:
         T = B * q_len
         self.splits = m.mla_sparse_decode_num_splits(T, H, topk, 0)
         ws = m.mla_decode_workspace_size(T, H, self.splits)
+        if fmt == "staged":
+            ws = m.mla_staged_workspace_size(T, H, topk, self.splits)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
         self.out = torch.empty(B, q_len, H, 512, dtype=torch.float32, device=device)
         self.lse = torch.empty(B, q_len, H, dtype=torch.float32, device=device)
@@ -105,14 +117,16 @@ class SparseWorkload:
 
     def decode(self, r):
         import nvfp4_compressed_mla_amd as m
-        m.mla_sparse_decode(self.q[r], self.cache, PAGE, self.block_table, self.idx[r],
-                            1.0 / math.sqrt(576.0), out=self.out, lse=self.lse,
-                            num_splits=self.splits, workspace=self.ws)
+        fn = {"nvfp4": m.mla_sparse_decode, "fp8": m.mla_fp8_sparse_decode,
+              "staged": m.mla_staged_sparse_decode}[self.fmt]
+        fn(self.q[r], self.cache, self.page, self.block_table, self.idx[r], 1.0 / math.sqrt(576.0),
+           out=self.out, lse=self.lse, num_splits=self.splits, workspace=self.ws)
 
     def append(self):
         import nvfp4_compressed_mla_amd as m
         if self.append_rows:
-            m.mla_nvfp4_quantize_append(self.new_lat, self.new_rope, self.new_slots, self.cache, PAGE)
+            fn = m.mla_fp8_append if self.fmt == "fp8" else m.mla_nvfp4_quantize_append
+            fn(self.new_lat, self.new_rope, self.new_slots, self.cache, self.page)
 
     def step(self, r):
         self.append()
@@ -121,10 +135,10 @@ class SparseWorkload:
     # algorithmic bytes / flops of the fused decode kernel for rotation r
     def kernel_bytes(self, r):
         T = self.B * self.q_len
-        return self.valid_pairs[r] * (352 + 4 + 4) + T * self.H * 576 * 2
+        return self.valid_pairs[r] * (self.row_bytes + 4 + 4) + T * self.H * 576 * 2
 
     def gathered_bytes(self, r):
-        return self.valid_pairs[r] * 352
+        return self.valid_pairs[r] * self.row_bytes
 
     def flops(self, r):
         return self.valid_pairs[r] * 2 * self.H * (576 + 512)
@@ -335,6 +349,8 @@ def run_config(wk, steps, warmup, prof_launches):
         "kernel_TFLOPs": round(fl / (kavg * 1e-3) / 1e12, 1),
         "kernel_mfma_frac": round(fl / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
         "splits": wk.splits,
+        **({"note": "fused_kernel_us is the FP8 decode kernel alone; us_per_launch includes the "
+                    "staging pass and the combine"} if getattr(wk, "fmt", "") == "staged" else {}),
     }
 
 
@@ -346,6 +362,9 @@ def main():
     ap.add_argument("--rotations", type=int, default=48)
     ap.add_argument("--prof-launches", type=int, default=64)
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
+    ap.add_argument("--extras", default="all",
+                    help="comma list of other configurations to run: pages, mtp, tiny, dense, "
+                         "mixed, three_way (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -421,7 +440,7 @@ def main():
         "gathered_pct_of_peak": round(100 * gathered / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"decode_kernel<{head_group_blocks(64)},false> (fused gather/decode/QK/softmax/PV)",
+            "kernel": f"decode_kernel<{head_group_blocks(64)},false,false> (fused gather/decode/QK/softmax/PV)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -436,44 +455,66 @@ def main():
         "context": {"pages_GB200_us_per_launch_15tok_16heads": 12.0},
     }
 
-    if not args.no_extra:
+    wanted = set() if args.no_extra or args.extras == "none" else (
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way"} if args.extras == "all"
+        else set(args.extras.split(",")))
+    if wanted:
         extra = {}
-        for name, mk in (
-            ("pages_shape_T15_H16", lambda: SparseWorkload("pages", 1, 15, 16, [149504], 2048, 0, 64, 1101, dev)),
-            ("mtp_B16_q15_H64", lambda: SparseWorkload("mtp", 16, 15, 64, [149504] * 16, 2048, 0, 6, 1002, dev)),
-            ("tiny_B1_H16_k256", lambda: SparseWorkload("tiny", 1, 1, 16, [4096], 256, 0, 8, 1000, dev)),
+        for name, key, mk in (
+            ("pages", "pages_shape_T15_H16", lambda: SparseWorkload("pages", 1, 15, 16, [149504], 2048, 0, 64, 1101, dev)),
+            ("mtp", "mtp_B16_q15_H64", lambda: SparseWorkload("mtp", 16, 15, 64, [149504] * 16, 2048, 0, 6, 1002, dev)),
+            ("tiny", "tiny_B1_H16_k256", lambda: SparseWorkload("tiny", 1, 1, 16, [4096], 256, 0, 8, 1000, dev)),
         ):
-            log(f"[bench] extra: {name}")
+            if name not in wanted:
+                continue
+            log(f"[bench] extra: {key}")
             w2 = mk()
-            extra[name] = run_config(w2, 192, 24, 32)
+            extra[key] = run_config(w2, 192, 24, 32)
             del w2
             torch.cuda.empty_cache()
-        log("[bench] extra: dense_B8_H64_146K")
-        dw = DenseWorkload(8, 64, 149504, 4096, 3, 1003, dev)
-        extra["dense_B8_H64_146K_split4096"] = run_config(dw, 48, 6, 24)
-        del dw
-        torch.cuda.empty_cache()
-        log("[bench] extra: mixed serving step")
-        from nvfp4_compressed_mla_amd import workloads as wl
-        mx = wl.named_workload("mixed")
-        # history lengths log-uniform in [4K, 200K]; the step appends 6144 rows to each request
-        mw = SparseWorkload("mixed", mx.B, 15, 64, [c + 6144 for c in mx.ctx], 2048, 6144, 4, 1004,
-                            dev, q_lens=mx.q_lens)
-        ms_mixed = time_steps(mw.step, mw.rot, 16, 4)
-        t0 = time.perf_counter()
-        for _ in range(8):
-            mw.append()
-        torch.cuda.synchronize()
-        ms_app = (time.perf_counter() - t0) * 1e3 / 8
-        extra["mixed_B64_step"] = {
-            "ms_per_step": round(ms_mixed, 4),
-            "append_rows": 6144 * 64,
-            "append_ms_eager": round(ms_app, 4),
-            "append_GBps_eager": round(6144 * 64 * (1152 + 352 + 8) / (ms_app * 1e-3) / 1e9, 1),
-            "decode": run_config(mw, 16, 4, 12),
-        }
-        del mw
-        torch.cuda.empty_cache()
+        if "dense" in wanted:
+            log("[bench] extra: dense_B8_H64_146K")
+            dw = DenseWorkload(8, 64, 149504, 4096, 3, 1003, dev)
+            extra["dense_B8_H64_146K_split4096"] = run_config(dw, 48, 6, 24)
+            del dw
+            torch.cuda.empty_cache()
+        if "mixed" in wanted:
+            log("[bench] extra: mixed serving step")
+            from nvfp4_compressed_mla_amd import workloads as wl
+            mx = wl.named_workload("mixed")
+            # history lengths log-uniform in [4K, 200K]; the step appends 6144 rows to each request
+            mw = SparseWorkload("mixed", mx.B, 15, 64, [c + 6144 for c in mx.ctx], 2048, 6144, 4, 1004,
+                                dev, q_lens=mx.q_lens)
+            ms_mixed = time_steps(mw.step, mw.rot, 16, 4)
+            t0 = time.perf_counter()
+            for _ in range(8):
+                mw.append()
+            torch.cuda.synchronize()
+            ms_app = (time.perf_counter() - t0) * 1e3 / 8
+            extra["mixed_B64_step"] = {
+                "ms_per_step": round(ms_mixed, 4),
+                "append_rows": 6144 * 64,
+                "append_ms_eager": round(ms_app, 4),
+                "append_GBps_eager": round(6144 * 64 * (1152 + 352 + 8) / (ms_app * 1e-3) / 1e9, 1),
+                "decode": run_config(mw, 16, 4, 12),
+            }
+            del mw
+            torch.cuda.empty_cache()
+        if "three_way" in wanted:
+            # the pages' three-way comparison: FP8 576-byte rows with the fused kernel, NVFP4 with
+            # the fused kernel, NVFP4 through the staged FP8 buffer
+            for shape, mk in (
+                ("pages_shape_T15_H16", lambda f: SparseWorkload("pages", 1, 15, 16, [149504], 2048, 0, 64, 1101, dev, fmt=f)),
+                ("batched_B32_H64", lambda f: SparseWorkload("batched", 32, 1, 64, [143360] * 32, 2048, 0, 24, 1001, dev, fmt=f)),
+            ):
+                cmp = {}
+                for f in ("fp8", "nvfp4", "staged"):
+                    log(f"[bench] three-way: {shape} {f}")
+                    w2 = mk(f)
+                    cmp[f] = run_config(w2, 192, 24, 32)
+                    del w2
+                    torch.cuda.empty_cache()
+                extra[f"three_way_{shape}"] = cmp
         result["extra"] = extra
 
     if not args.no_cpu_baseline:

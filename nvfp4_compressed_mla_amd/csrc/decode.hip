@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 #include "nvfp4_device.h"
 
@@ -176,31 +178,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   if (math) {
     // Converted here (FP16; softmax_scale * log2(e) is applied to the scores), while the
     // producer waves compact the index list.
-    uint4v qraw[kChunks];                     // bf16 queries: one 16-byte load per chunk
-    if (qk_wave && !a.q_fp32) {
+    if (!a.q_fp32) {
+      uint4v qraw[kChunks];                   // bf16 queries: one 16-byte load per chunk
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) qraw[c] = *(const uint4v*)((const uint16_t*)a.q + qrow + 32 * c);
-    }
+      for (int c = 0; c < kChunks; ++c) qraw[c] = uint4v{0u, 0u, 0u, 0u};
+      if (qk_wave) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      float f[8];
-      if (!a.q_fp32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = __uint_as_float(qraw[c][i] << 16);
-          f[2 * i + 1] = __uint_as_float(qraw[c][i] & 0xFFFF0000u);
-        }
-      } else if (qk_wave) {                  // fp32 queries (small launches): load as needed
-        const float4v lo = *(const float4v*)((const float*)a.q + qrow + 32 * c);
-        const float4v hi = *(const float4v*)((const float*)a.q + qrow + 32 * c + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+        for (int c = 0; c < kChunks; ++c) qraw[c] = *(const uint4v*)((const uint16_t*)a.q + qrow + 32 * c);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[c][i] = (_Float16)f[i];
+      for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qf[c][2 * i] = (_Float16)__uint_as_float(qraw[c][i] << 16);
+          qf[c][2 * i + 1] = (_Float16)__uint_as_float(qraw[c][i] & 0xFFFF0000u);
+        }
+    } else {                                  // fp32 queries (small launches)
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        float4v lo = float4v{0.f, 0.f, 0.f, 0.f}, hi = lo;
+        if (qk_wave) {
+          lo = *(const float4v*)((const float*)a.q + qrow + 32 * c);
+          hi = *(const float4v*)((const float*)a.q + qrow + 32 * c + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qf[c][i] = (_Float16)lo[i]; qf[c][4 + i] = (_Float16)hi[i]; }
+      }
     }
   }
 
@@ -359,72 +362,79 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if constexpr (!FP8) tile_offsets(3, next_o16);
     float m_run = -INFINITY, l_run = 0.0f;     // running max (log2 units), partial sum
     const int kslot = ((kg << 4) + (l16 ^ ((kg & 1) << 2))) << 4;   // QK A-fragment slot
-    for (int i = 0; i <= n_tiles; ++i) {
-      if (qk_wave && i < n_tiles) {
-        const uint8_t* dt = dec[i % kDecSlots];
-        float4v acc[2][2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) { acc[rb][0] = float4v{0.f, 0.f, 0.f, 0.f}; acc[rb][1] = acc[rb][0]; }
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c)
-#pragma unroll
+    // One loop per kind of math wave (head-block owners and, when a group has fewer than four
+    // head blocks, gather-only waves), so that neither carries the other's registers.
+    auto math_loop = [&](auto qkw_tag) {
+      constexpr bool QKW = decltype(qkw_tag)::value;
+      for (int i = 0; i <= n_tiles; ++i) {
+        if (QKW && i < n_tiles) {
+          const uint8_t* dt = dec[i % kDecSlots];
+          float4v acc[2][2];
+  #pragma unroll
+          for (int rb = 0; rb < 2; ++rb) { acc[rb][0] = float4v{0.f, 0.f, 0.f, 0.f}; acc[rb][1] = acc[rb][0]; }
+  #pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+  #pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const half8v kf = *(const half8v*)(dt + (rb * kChunks + c) * kFragBytes + kslot);
+              acc[rb][c & 1] = mfma16(kf, qf[c], acc[rb][c & 1]);
+            }
+          // Issue order: 8 fragment reads ahead of the MFMAs, then one read per MFMA, so LDS
+          // latency stays hidden behind the matrix work.
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  #pragma unroll
+          for (int k = 0; k < 2 * kChunks - 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          uint32_t cur_o16[3] = {next_o16[0], next_o16[1], next_o16[2]};
+          if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
+          float sv[8];
+          float mx = -INFINITY;
+  #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            const half8v kf = *(const half8v*)(dt + (rb * kChunks + c) * kFragBytes + kslot);
-            acc[rb][c & 1] = mfma16(kf, qf[c], acc[rb][c & 1]);
+            const float4v sc = acc[rb][0] + acc[rb][1];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = i * kTileRows + 16 * rb + 4 * kg + e;
+              sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
+              mx = fmaxf(mx, sv[4 * rb + e]);
+            }
           }
-        // Issue order: 8 fragment reads ahead of the MFMAs, then one read per MFMA, so LDS
-        // latency stays hidden behind the matrix work.
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int k = 0; k < 2 * kChunks - 8; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        uint32_t cur_o16[3] = {next_o16[0], next_o16[1], next_o16[2]};
-        if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
-        float sv[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const float4v sc = acc[rb][0] + acc[rb][1];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = i * kTileRows + 16 * rb + 4 * kg + e;
-            sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[4 * rb + e]);
+          mx = group4_max(mx);
+          // The running max moves lazily: only when a tile's max exceeds it by more than 2^8, so
+          // the probabilities stay <= 256 (exact range for FP16) and O is rescaled only then.
+          const bool move = mx > m_run + 8.0f;        // also true on the first tile (m_run = -inf)
+          const float m_new = move ? mx : m_run;
+          const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          half4v pf[2];
+          float psum = 0.0f;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+            pf[e >> 2][e & 3] = pv;
+            psum += (float)pv;
           }
+          l_run = l_run * alpha + psum;
+          m_run = m_new;
+          uint8_t* prow_p = pbuf[i & 1] + (16 * w + l16) * kPStride;
+          *(half4v*)(prow_p + 8 * kg) = pf[0];           // rows 4kg..4kg+3
+          *(half4v*)(prow_p + 32 + 8 * kg) = pf[1];      // rows 16+4kg..
+          const uint64_t any = __ballot(move && i > 0);
+          if (lane == 0) flag_s[i & 1][w] = any != 0ull;
+          if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
+          if constexpr (!FP8) issue_tile(i + 3, cur_o16);
         }
-        mx = group4_max(mx);
-        // The running max moves lazily: only when a tile's max exceeds it by more than 2^8, so
-        // the probabilities stay <= 256 (exact range for FP16) and O is rescaled only then.
-        const bool move = mx > m_run + 8.0f;        // also true on the first tile (m_run = -inf)
-        const float m_new = move ? mx : m_run;
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        half4v pf[2];
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
-          pf[e >> 2][e & 3] = pv;
-          psum += (float)pv;
+        if constexpr (!FP8) {
+          if (!(QKW && i < n_tiles)) { issue_tile(i + 3, next_o16); tile_offsets(i + 4, next_o16); }
+          wait_tiles(1);
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        uint8_t* prow_p = pbuf[i & 1] + (16 * w + l16) * kPStride;
-        *(half4v*)(prow_p + 8 * kg) = pf[0];           // rows 4kg..4kg+3
-        *(half4v*)(prow_p + 32 + 8 * kg) = pf[1];      // rows 16+4kg..
-        const uint64_t any = __ballot(move && i > 0);
-        if (lane == 0) flag_s[i & 1][w] = any != 0ull;
-        if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
-        if constexpr (!FP8) issue_tile(i + 3, cur_o16);
+        lds_barrier();
       }
-      if constexpr (!FP8) {
-        if (!(qk_wave && i < n_tiles)) { issue_tile(i + 3, next_o16); tile_offsets(i + 4, next_o16); }
-        wait_tiles(1);
-      }
-      lds_barrier();
-    }
+    };
+    if (qk_wave) math_loop(std::true_type{});
+    else math_loop(std::false_type{});
     wait_vmcnt<0>();                          // no gather may still target LDS at exit
     if (qk_wave) {
       const float lt = group4_sum(l_run);

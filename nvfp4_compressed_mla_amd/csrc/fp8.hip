@@ -78,6 +78,10 @@ __device__ __forceinline__ uint4v group_to_fp8(uint2v codes, uint2v t, uint32_t 
 // the staged index list gets e (or -1). staged_bt maps page p of "request" tok to page
 // tok*(topk_pad/64) + p, so the FP8 kernel reads the staged rows through ordinary paging.
 // 16 lanes per row: lane i converts latent groups i and i+16 and copies 4 rope bytes.
+// kStageRows: list entries in flight per 16-lane group (more for large launches, where the
+// workgroups outnumber what the chip holds at once; one for small ones, to spread the latency
+// chains over more workgroups)
+template <int kStageRows>
 __global__ __launch_bounds__(256) void stage_fp8_kernel(
     const uint8_t* __restrict__ cache, int64_t page_stride, int64_t cache_bytes,
     const int32_t* __restrict__ block_table, int32_t max_pages,
@@ -85,49 +89,77 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(
     int64_t total_rows, uint8_t* __restrict__ staged, int32_t* __restrict__ staged_idx,
     int32_t* __restrict__ staged_bt) {
   __shared__ uint2v tab[128];
-  {
-    // tab[s] byte m = E4M3(E2M1 magnitude m * value of scale byte s), s = 0..127
-    const int s = threadIdx.x >> 1, part = threadIdx.x & 1;
-    const float sv = e4m3_to_float((uint32_t)s);
-    const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) word |= e4m3_encode(mags[4 * part + k] * sv) << (8 * k);
-    ((uint32_t*)tab)[2 * s + part] = word;
-  }
-  __syncthreads();
-
   const int li = threadIdx.x & 15;
   const int pages2 = topk_pad >> 6;
-  for (int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); r < total_rows;
-       r += (int64_t)gridDim.x * 16) {
-    const int64_t tok = r / topk;
-    const int e = (int)(r - tok * topk);
-    const int b = (int)(tok / q_len);
-    const int j = topk_idx[r];
-    int64_t off = -1;
-    if (j >= 0 && (int64_t)j < (int64_t)max_pages * kPageRows) {
-      const int pg = block_table[(int64_t)b * max_pages + (j >> 6)];
-      if (pg >= 0) {
-        const int64_t o = (int64_t)pg * page_stride + (int64_t)(j & 63) * kRowBytes;
-        if (o + kRowBytes <= cache_bytes) off = o;
+  const int64_t r_step = (int64_t)gridDim.x * 16;
+  const int group = threadIdx.x >> 4;
+  // the trip count depends on the workgroup only (every thread reaches the barrier below)
+  for (int64_t base = (int64_t)blockIdx.x * 16; base < total_rows; base += r_step * kStageRows) {
+    const int64_t rb = base + group;
+    // kStageRows entries rb, rb + r_step, ...: all index loads, then all block-table loads,
+    // then all row loads, so their latencies overlap
+    int j[kStageRows], pg[kStageRows];
+    int64_t off[kStageRows];
+#pragma unroll
+    for (int k = 0; k < kStageRows; ++k) {
+      const int64_t r = rb + k * r_step;
+      j[k] = r < total_rows ? topk_idx[r] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kStageRows; ++k) {
+      const int64_t r = rb + k * r_step;
+      const bool in = j[k] >= 0 && (int64_t)j[k] < (int64_t)max_pages * kPageRows;
+      const int b = (int)((in ? r : 0) / topk / q_len);
+      pg[k] = in ? block_table[(int64_t)b * max_pages + (j[k] >> 6)] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kStageRows; ++k) {
+      const int64_t o = (int64_t)pg[k] * page_stride + (int64_t)(j[k] & 63) * kRowBytes;
+      off[k] = (pg[k] >= 0 && o + kRowBytes <= cache_bytes) ? o : -1;
+    }
+    uint2v c0[kStageRows], c1[kStageRows];
+    uint32_t s0[kStageRows], s1[kStageRows], rp[kStageRows];
+#pragma unroll
+    for (int k = 0; k < kStageRows; ++k) {
+      if (off[k] >= 0) {
+        const uint8_t* src = cache + off[k];
+        c0[k] = *(const uint2v*)(src + 8 * li);
+        c1[k] = *(const uint2v*)(src + 128 + 8 * li);
+        s0[k] = src[kScaleOff + li];
+        s1[k] = src[kScaleOff + 16 + li];
+        rp[k] = *(const uint32_t*)(src + kRopeOff + 4 * li);
       }
     }
-    if (li == 0) {
-      staged_idx[r] = off >= 0 ? e : -1;
-      if ((e & 63) == 0) staged_bt[tok * pages2 + (e >> 6)] = (int32_t)(tok * pages2 + (e >> 6));
+    if (base == (int64_t)blockIdx.x * 16) {
+      // tab[s] byte m = E4M3(E2M1 magnitude m * value of scale byte s), s = 0..127; built once,
+      // while the first entries' loads are in flight
+      const int s = threadIdx.x >> 1, part = threadIdx.x & 1;
+      const float sv = e4m3_to_float((uint32_t)s);
+      const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) word |= e4m3_encode(mags[4 * part + k] * sv) << (8 * k);
+      ((uint32_t*)tab)[2 * s + part] = word;
+      __syncthreads();
     }
-    if (off < 0) continue;
-    const uint8_t* src = cache + off;
-    const uint2v c0 = *(const uint2v*)(src + 8 * li);
-    const uint2v c1 = *(const uint2v*)(src + 128 + 8 * li);
-    const uint32_t s0 = src[kScaleOff + li], s1 = src[kScaleOff + 16 + li];
-    const uint32_t rp = *(const uint32_t*)(src + kRopeOff + 4 * li);
-    const uint32_t f0 = (s0 & 0x80u) ? 0x80808080u : 0u, f1 = (s1 & 0x80u) ? 0x80808080u : 0u;
-    uint8_t* dst = staged + (tok * topk_pad + e) * kFp8RowBytes;
-    *(uint4v*)(dst + 16 * li) = group_to_fp8(c0, tab[s0 & 127u], f0);
-    *(uint4v*)(dst + 256 + 16 * li) = group_to_fp8(c1, tab[s1 & 127u], f1);
-    *(uint32_t*)(dst + kLatent + 4 * li) = rp;
+#pragma unroll
+    for (int k = 0; k < kStageRows; ++k) {
+      const int64_t r = rb + k * r_step;
+      if (r >= total_rows) break;
+      const int64_t tok = r / topk;
+      const int e = (int)(r - tok * topk);
+      if (li == 0) {
+        staged_idx[r] = off[k] >= 0 ? e : -1;
+        if ((e & 63) == 0) staged_bt[tok * pages2 + (e >> 6)] = (int32_t)(tok * pages2 + (e >> 6));
+      }
+      if (off[k] >= 0) {
+        const uint32_t f0 = (s0[k] & 0x80u) ? 0x80808080u : 0u, f1 = (s1[k] & 0x80u) ? 0x80808080u : 0u;
+        uint8_t* dst = staged + (tok * topk_pad + e) * kFp8RowBytes;
+        *(uint4v*)(dst + 16 * li) = group_to_fp8(c0[k], tab[s0[k] & 127u], f0);
+        *(uint4v*)(dst + 256 + 16 * li) = group_to_fp8(c1[k], tab[s1[k] & 127u], f1);
+        *(uint32_t*)(dst + kLatent + 4 * li) = rp[k];
+      }
+    }
   }
 }
 
@@ -149,13 +181,21 @@ hipError_t launch_stage_fp8(const void* cache, int64_t page_stride, int64_t cach
                             int32_t* staged_idx, int32_t* staged_bt, hipStream_t stream) {
   const int32_t topk_pad = (topk + 63) & ~63;
   const int64_t total = (int64_t)T * topk;
-  int64_t blocks = (total + 15) / 16;
-  const int64_t max_blocks = 256 * 16;
+  const bool big = total >= 65536;
+  const int rows = big ? 4 : 1;
+  int64_t blocks = (total + 16 * rows - 1) / (16 * rows);
+  const int64_t max_blocks = 256 * 8;
   if (blocks > max_blocks) blocks = max_blocks;
-  hipLaunchKernelGGL(stage_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint8_t*)cache, page_stride, cache_bytes, block_table, max_pages,
-                     topk_idx, topk, q_len, topk_pad, total, (uint8_t*)staged, staged_idx,
-                     staged_bt);
+  if (big)
+    hipLaunchKernelGGL(stage_fp8_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint8_t*)cache, page_stride, cache_bytes, block_table, max_pages,
+                       topk_idx, topk, q_len, topk_pad, total, (uint8_t*)staged, staged_idx,
+                       staged_bt);
+  else
+    hipLaunchKernelGGL(stage_fp8_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint8_t*)cache, page_stride, cache_bytes, block_table, max_pages,
+                       topk_idx, topk, q_len, topk_pad, total, (uint8_t*)staged, staged_idx,
+                       staged_bt);
   return hipGetLastError();
 }
 
