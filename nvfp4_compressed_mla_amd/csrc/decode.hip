@@ -171,13 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int b = tok / a.q_len, t = tok % a.q_len;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // ---- math waves: start the query loads of head block w (they overlap the compaction) -------
+  // ---- queries of head block w (math waves) -------------------------------------------------
   const bool qk_wave = math && w < NH;
   const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kg;
   half8v qf[kChunks];                         // queries as 18 FP16 fragments (math waves)
-  if (math) {
-    // Converted here (FP16; softmax_scale * log2(e) is applied to the scores), while the
-    // producer waves compact the index list.
+  // Loaded after the index compaction (their traffic would otherwise slow its dependent loads
+  // down), while the producers' first gathers are in flight; converted to FP16 (softmax_scale *
+  // log2(e) is applied to the scores).
+  auto load_q = [&]() {
     if (!a.q_fp32) {
       uint4v qraw[kChunks];                   // bf16 queries: one 16-byte load per chunk
 #pragma unroll
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         for (int i = 0; i < 4; ++i) { qf[c][i] = (_Float16)lo[i]; qf[c][4 + i] = (_Float16)hi[i]; }
       }
     }
-  }
+  };
 
   // ---- rows of this split (producer waves) --------------------------------------------------
   int n_rows = 0;
@@ -308,20 +309,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     const int p = min(k * 256 + (w & 3) * 64 + lane, kRawPieces - 1);
     pk[k] = ((uint32_t)(p / 22) << 16) | (uint32_t)((p % 22) * 16);
   }
+  // Offset (16-byte units) of row `row` of this split, kInvalid past the end or without a page.
+  auto row_o16 = [&](int row) -> uint32_t {
+    const bool ok = row < n_rows;
+    if constexpr (!DENSE) {
+      return ok ? rowoff[row] : kInvalid;
+    } else {
+      const int pos = p0 + (ok ? row : 0);
+      const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
+      const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
+      return (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
+    }
+  };
   auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int row = tile * kTileRows + (int)(pk[k] >> 16);
-      const bool ok = row < n_rows;
-      if constexpr (!DENSE) {
-        o16[k] = ok ? rowoff[row] : kInvalid;
-      } else {
-        const int pos = p0 + (ok ? row : 0);
-        const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-        const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
-        o16[k] = (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
-      }
-    }
+    for (int k = 0; k < 3; ++k) o16[k] = row_o16(tile * kTileRows + (int)(pk[k] >> 16));
   };
   auto issue_tile = [&](int tile, const uint32_t (&o16)[3]) {
     uint8_t* dst = raw[tile % kRawSlots];
@@ -344,19 +346,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   if (math) {
     // ================================ math waves ================================================
-    // The query conversion must finish before the first gather: a later wait for the query
-    // loads would otherwise also wait for the gathers, which share the vector-memory counter.
+    // The first three tiles are gathered by the producer waves, so that no gather of this wave
+    // is in flight while its query loads are waited for (they share the vector-memory counter).
+    load_q();
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) asm volatile("" : "+v"(qf[c]));
-    if constexpr (!FP8) {
-      uint32_t o16[3];
-      tile_offsets(0, o16); issue_tile(0, o16);
-      tile_offsets(1, o16); issue_tile(1, o16);
-      tile_offsets(2, o16); issue_tile(2, o16);
-    }
-    if constexpr (!FP8) wait_tiles(2);
     lds_barrier();                            // prologue: tile 0 in LDS
-    if constexpr (!FP8) wait_tiles(1);
     lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
     uint32_t next_o16[3] = {kInvalid, kInvalid, kInvalid};   // row offsets of the next tile to gather
     if constexpr (!FP8) tile_offsets(3, next_o16);
@@ -519,8 +514,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       lds_barrier();                          // prologue (same barrier count as the gathers)
       if (n_tiles > 0) fp8_store(0, f0);
     } else {
+      // Tiles 0..2: piece q = k*512 + ptid (k = 0, 1; only waves 0..2 have a k = 1 piece, as a
+      // tile has 704 pieces), issued right after the compaction.
+      const int np = (pw < 3) ? 2 : 1;
+      auto prod_issue = [&](int tile) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (k == 1 && np == 1) break;
+          const int q = k * 512 + ptid;
+          const uint32_t pb = (uint32_t)((q % 22) * 16);
+          const uint32_t o16 = row_o16(tile * kTileRows + q / 22);
+          const uint8_t* src = (o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 + pb : g_zero_row + pb;
+          gather16_to_lds(src, raw[tile % kRawSlots] + (k * 512 + pw * 64) * 16);
+        }
+      };
+      prod_issue(0);
+      prod_issue(1);
+      prod_issue(2);
+      if (np == 2) wait_vmcnt<4>(); else wait_vmcnt<2>();      // tile 0 landed
       lds_barrier();                          // prologue: tile 0 in LDS
       if (n_tiles > 0) decode_tile(0);
+      if (np == 2) wait_vmcnt<2>(); else wait_vmcnt<1>();      // tile 1 landed
     }
     lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
     // Transposing-read offsets (V operand of PV): the lane supplies 4 dims
@@ -570,8 +584,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       if constexpr (FP8) {
         if (dec_next) fp8_store(i + 1, f1);
         f1 = f2;
-      } else if (dec_next) {
-        decode_store(i + 1, din);
+      } else {
+        if (dec_next) decode_store(i + 1, din);
+        if (i == 0) wait_vmcnt<0>();          // tile 2 (gathered in the prologue) landed
       }
       lds_barrier();
     }
@@ -622,10 +637,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
 // Merge the n_split partial (o_s, lse_s) of each (token, head) in split order:
 // M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
-// A thread owns one dim of 4 heads, the 8-byte FP16 unit the decode kernel stored; splits are taken
-// 8 at a time with every load of a chunk issued before its first use.
+// A thread owns one dim of 4 heads, the 8-byte FP16 unit the decode kernel stored. SC > 0 handles
+// up to SC splits with every load issued in one round (one memory latency); SC == 0 handles any
+// split count, 8 splits at a time.
 constexpr int kCombineChunk = 8;
 
+template <int SC>
 __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int32_t S,
                                                       const _Float16* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
@@ -646,38 +663,55 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   const int64_t split_stride = (int64_t)H * kLatent;
   const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 32 + ng) * 64 + lane) * 4;
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
-  float4v M = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
-    float4v v[kCombineChunk];
-#pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j)
-      v[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)(s0 + j) * H)
-                          : float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], v[j][e]);
-  }
+  const float4v ninf = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float4v M = ninf;
   float4v acc = float4v{0.f, 0.f, 0.f, 0.f}, wsum = acc;
-  for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
-    float4v ls[kCombineChunk], ov[kCombineChunk];
+  auto merge = [&](const float4v& ls, const half4v& hv) {
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j) {
-      const int s = min(s0 + j, S - 1);
-      ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H)
-                           : float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      const half4v hv = *(const half4v*)(op + s * split_stride);
-      ov[j] = float4v{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+    for (int e = 0; e < 4; ++e) {
+      const float wgt = (ls[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((ls[e] - M[e]) * 1.4426950408889634f);
+      acc[e] += wgt * (float)hv[e];
+      wsum[e] += wgt;
+    }
+  };
+  if constexpr (SC > 0) {
+    float4v ls[SC];
+    half4v ov[SC];
+#pragma unroll
+    for (int j = 0; j < SC; ++j) {
+      const int s = min(j, S - 1);                        // splits past S: weight 0
+      ls[j] = (j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
+      ov[j] = *(const half4v*)(op + s * split_stride);
     }
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j)
+    for (int j = 0; j < SC; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float wgt = (ls[j][e] == -INFINITY) ? 0.0f
-                                                  : __builtin_amdgcn_exp2f((ls[j][e] - M[e]) * 1.4426950408889634f);
-        acc[e] += wgt * ov[j][e];
-        wsum[e] += wgt;
+      for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], ls[j][e]);
+#pragma unroll
+    for (int j = 0; j < SC; ++j) merge(ls[j], ov[j]);
+  } else {
+    for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+      float4v v[kCombineChunk];
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j)
+        v[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)(s0 + j) * H) : ninf;
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], v[j][e]);
+    }
+    for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+      float4v ls[kCombineChunk];
+      half4v ov[kCombineChunk];
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) {
+        const int s = min(s0 + j, S - 1);
+        ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
+        ov[j] = *(const half4v*)(op + s * split_stride);
       }
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) merge(ls[j], ov[j]);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -722,8 +756,15 @@ hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16*
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
   const int32_t total = T * (H / 16) * 8;
   const int32_t per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
-                     n_split, ws_o, ws_lse, out, lse, per_xcd, total);
+  if (n_split <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
+                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
+  else if (n_split <= 16)
+    hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
+                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
+                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
   return hipGetLastError();
 }
 
