@@ -281,6 +281,42 @@ def counters_traffic(src_hash):
         return None
 
 
+# ---- block transfer between multi-layer pools --------------------------------------------------
+
+def kv_transfer(dev, n_layers=64, ctx=204800, pool_blocks=16000, reps=5):
+    """One 200K-token request's blocks (all layers) copied between two pools, block-major and
+    layer-major, in one launch each; contiguous regions (transfer descriptors) per layout."""
+    import torch
+    import nvfp4_compressed_mla_amd as m
+    page = PAGE
+    n_blk = ctx // 64
+    g = torch.Generator().manual_seed(2024)
+    sb = torch.randperm(pool_blocks, generator=g)[:n_blk].to(torch.int32)
+    db = torch.randperm(pool_blocks, generator=g)[:n_blk].to(torch.int32)
+    src = torch.empty(pool_blocks * n_layers * page, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(7)
+    sbd, dbd = sb.to(dev), db.to(dev)
+    moved = n_blk * n_layers * page
+    res = {"layers": n_layers, "blocks": n_blk, "bytes_moved": moved}
+    for name, layout in (("block_major", m.MLA_LAYOUT_BLOCK_MAJOR), ("layer_major", m.MLA_LAYOUT_LAYER_MAJOR)):
+        m.mla_copy_kv_blocks(src, dst, layout, n_layers, page, sbd, dbd)       # warm
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            m.mla_copy_kv_blocks(src, dst, layout, n_layers, page, sbd, dbd)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        res[name] = {"descriptors": m.mla_kv_transfer_regions(layout, n_layers, page, pool_blocks, sb.numpy()),
+                     "ms": round(ms, 3), "moved_GBps": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "hbm_GBps_read_plus_write": round(2 * moved / (ms * 1e-3) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---- CPU oracle baseline -----------------------------------------------------------------------
 
 def cpu_baseline(wk, budget_s=12.0):
@@ -364,7 +400,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way (default all; 'none' = --no-extra)")
+                         "mixed, three_way, kv_transfer (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -456,7 +492,7 @@ def main():
     }
 
     wanted = set() if args.no_extra or args.extras == "none" else (
-        {"pages", "mtp", "tiny", "dense", "mixed", "three_way"} if args.extras == "all"
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "kv_transfer"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
         extra = {}
@@ -515,6 +551,8 @@ def main():
                     del w2
                     torch.cuda.empty_cache()
                 extra[f"three_way_{shape}"] = cmp
+        if "kv_transfer" in wanted:
+            extra["kv_transfer_200K"] = kv_transfer(dev)
         result["extra"] = extra
 
     if not args.no_cpu_baseline:

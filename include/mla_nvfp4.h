@@ -195,6 +195,35 @@ mla_status mla_staged_sparse_decode(const void* q, mla_dtype q_dtype,
                                     int32_t num_splits, float* out, float* lse,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Multi-layer page pools and block transfer --------------------------------------------
+ * Page section "Changing the layout to reduce fragmentation": a layer-major pool (LBHNC) stores
+ * each layer's pages on their own, so a 64-token block spans one region per layer; a block-major
+ * pool (BLHNC) keeps the pages of all layers of a block side by side. A pool holds pool_blocks
+ * blocks x n_layers pages of page_bytes bytes (64 * 352 for one layer of NVFP4 rows):
+ *   block-major: page (b, l) at byte (b * n_layers + l) * page_bytes;
+ *   layer-major: page (b, l) at byte (l * pool_blocks + b) * page_bytes.
+ * Layer l of a block-major pool is the paged cache at pool + l * page_bytes with
+ * page_stride_bytes = n_layers * page_bytes (layer-major: pool + l * pool_blocks * page_bytes,
+ * page_stride_bytes = page_bytes), as the decode entry points take it. */
+typedef enum { MLA_LAYOUT_BLOCK_MAJOR = 0, MLA_LAYOUT_LAYER_MAJOR = 1 } mla_kv_layout;
+
+/* Copy every layer's page of block src_blocks[i] of src_pool to block dst_blocks[i] of dst_pool,
+ * for i < n_blocks, in one launch. Both pools have the given layout; their block counts are
+ * pool_bytes / (n_layers * page_bytes) (the sizes must be whole multiples). src_blocks and
+ * dst_blocks are int32 device arrays; a block id outside its pool skips that pair. Pools 16-byte
+ * aligned, page_bytes a multiple of 16. Overlapping source and destination pages race. */
+mla_status mla_copy_kv_blocks(const void* src_pool, int64_t src_pool_bytes,
+                              void* dst_pool, int64_t dst_pool_bytes,
+                              mla_kv_layout layout, int32_t n_layers, int64_t page_bytes,
+                              const int32_t* src_blocks, const int32_t* dst_blocks,
+                              int32_t n_blocks, hipStream_t stream);
+
+/* Host helper: the number of contiguous byte ranges (transfer descriptors) that cover all pages
+ * of the given blocks (int32 HOST array) in a pool of pool_blocks blocks, touching ranges merged.
+ * Returns -1 for invalid arguments or a block id outside the pool. */
+int64_t mla_kv_transfer_regions(mla_kv_layout layout, int32_t n_layers, int64_t page_bytes,
+                                int64_t pool_blocks, const int32_t* blocks, int32_t n_blocks);
+
 /* Test hook, off the hot path: decode the rows at `slots` (int64 [n]) into fp32 [n, 576]
  * (latent then rope), through the same on-chip decoder the attention kernels use. Values are
  * exact. Slots outside the cache produce zeros. */

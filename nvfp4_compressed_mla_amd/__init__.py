@@ -5,8 +5,12 @@ this package holds its build script, the ctypes binding and the seeded workload 
 """
 
 from ._lib import (  # noqa: F401
+    MLA_LAYOUT_BLOCK_MAJOR,
+    MLA_LAYOUT_LAYER_MAJOR,
     MlaError,
     load_library,
+    mla_copy_kv_blocks,
+    mla_kv_transfer_regions,
     mla_decode_workspace_size,
     mla_dense_decode,
     mla_dense_decode_num_splits,

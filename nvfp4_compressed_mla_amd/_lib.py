@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libmla_nvfp4.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_BF16, MLA_FP32 = 0, 1
+MLA_LAYOUT_BLOCK_MAJOR, MLA_LAYOUT_LAYER_MAJOR = 0, 1
 ROW_BYTES = 352
 FP8_ROW_BYTES = 576
 PAGE_ROWS = 64
@@ -35,6 +36,8 @@ EXPORTED = [
     "mla_nvfp4_stage_fp8",
     "mla_staged_workspace_size",
     "mla_staged_sparse_decode",
+    "mla_copy_kv_blocks",
+    "mla_kv_transfer_regions",
     "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
@@ -94,6 +97,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_staged_workspace_size.restype = sz
     lib.mla_staged_sparse_decode.argtypes = lib.mla_sparse_decode.argtypes
     lib.mla_staged_sparse_decode.restype = ctypes.c_int
+    lib.mla_copy_kv_blocks.argtypes = [vp, i64, vp, i64, ctypes.c_int, i32, i64, vp, vp, i32, vp]
+    lib.mla_copy_kv_blocks.restype = ctypes.c_int
+    lib.mla_kv_transfer_regions.argtypes = [ctypes.c_int, i32, i64, i64, vp, i32]
+    lib.mla_kv_transfer_regions.restype = i64
     lib.mla_set_timing_events.argtypes = [vp, vp]
     lib.mla_set_timing_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -374,6 +381,37 @@ def mla_nvfp4_stage_fp8(kv_cache, page_stride_bytes, block_table, topk_idx, stag
         block_table.shape[1], _ptr(topk_idx), topk, B, q_len, _ptr(staged_rows), _ptr(staged_idx),
         _ptr(staged_block_table), _stream(stream)))
     return staged_rows, staged_idx, staged_block_table
+
+
+def mla_copy_kv_blocks(src_pool, dst_pool, layout: int, n_layers: int, page_bytes: int,
+                       src_blocks, dst_blocks, stream=None):
+    """Copy all layer pages of src_blocks[i] of src_pool to dst_blocks[i] of dst_pool (uint8
+    device pools of the given layout, int32 device block lists)."""
+    torch = _torch()
+    _require(src_pool, "src_pool", torch.uint8)
+    _require(dst_pool, "dst_pool", torch.uint8)
+    _require(src_blocks, "src_blocks", torch.int32)
+    _require(dst_blocks, "dst_blocks", torch.int32)
+    if src_blocks.numel() != dst_blocks.numel() or not src_blocks.is_contiguous() \
+            or not dst_blocks.is_contiguous():
+        raise ValueError("block lists must be contiguous and of equal length")
+    _check(load_library().mla_copy_kv_blocks(
+        _ptr(src_pool), src_pool.numel(), _ptr(dst_pool), dst_pool.numel(), int(layout),
+        int(n_layers), int(page_bytes), _ptr(src_blocks), _ptr(dst_blocks), src_blocks.numel(),
+        _stream(stream)))
+
+
+def mla_kv_transfer_regions(layout: int, n_layers: int, page_bytes: int, pool_blocks: int,
+                            blocks) -> int:
+    """Contiguous byte ranges covering all pages of ``blocks`` (host sequence of block ids)."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32))
+    n = int(load_library().mla_kv_transfer_regions(
+        int(layout), int(n_layers), int(page_bytes), int(pool_blocks),
+        arr.ctypes.data_as(ctypes.c_void_p), arr.size))
+    if n < 0:
+        raise MlaError(MLA_ERR_INVALID_ARG, "invalid layout arguments or block id outside the pool")
+    return n
 
 
 def mla_set_timing_events(start, stop) -> None:

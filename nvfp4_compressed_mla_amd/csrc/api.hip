@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronizes; every check runs before any HIP call.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -439,6 +440,60 @@ mla_status mla_staged_sparse_decode(const void* q, mla_dtype q_dtype, const void
                             (int64_t)T * topk_pad * MLA_FP8_ROW_BYTES, (const int32_t*)(ws + l.bt),
                             topk_pad / 64, (const int32_t*)(ws + l.idx), topk, (int32_t)T, 1, H,
                             softmax_scale, num_splits, out, lse, ws + l.dec, l.total - l.dec, stream);
+}
+
+mla_status mla_copy_kv_blocks(const void* src_pool, int64_t src_pool_bytes, void* dst_pool,
+                              int64_t dst_pool_bytes, mla_kv_layout layout, int32_t n_layers,
+                              int64_t page_bytes, const int32_t* src_blocks,
+                              const int32_t* dst_blocks, int32_t n_blocks, hipStream_t stream) {
+  if (layout != MLA_LAYOUT_BLOCK_MAJOR && layout != MLA_LAYOUT_LAYER_MAJOR)
+    return fail(MLA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
+  if (n_layers < 1 || page_bytes < 16 || page_bytes % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "n_layers must be >= 1 and page_bytes a positive multiple of 16");
+  if (n_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "n_blocks must be >= 0");
+  const int64_t block_bytes = (int64_t)n_layers * page_bytes;
+  if (src_pool_bytes < block_bytes || dst_pool_bytes < block_bytes ||
+      src_pool_bytes % block_bytes != 0 || dst_pool_bytes % block_bytes != 0)
+    return fail(MLA_ERR_INVALID_ARG, "pool sizes must be whole multiples of n_layers * page_bytes");
+  if (n_blocks == 0) return hip_status(hipSuccess, "");
+  if (!src_pool || !dst_pool || !src_blocks || !dst_blocks)
+    return fail(MLA_ERR_INVALID_ARG, "null pool or block list");
+  if (!aligned(src_pool, 16) || !aligned(dst_pool, 16) || !aligned(src_blocks, 4) || !aligned(dst_blocks, 4))
+    return fail(MLA_ERR_INVALID_ARG, "pools must be 16-byte and block lists 4-byte aligned");
+  return hip_status(mla::launch_copy_pages(src_pool, src_pool_bytes / block_bytes, dst_pool,
+                                           dst_pool_bytes / block_bytes, (int32_t)layout, n_layers,
+                                           page_bytes, src_blocks, dst_blocks, n_blocks, stream),
+                    "copy_kv_blocks launch");
+}
+
+int64_t mla_kv_transfer_regions(mla_kv_layout layout, int32_t n_layers, int64_t page_bytes,
+                                int64_t pool_blocks, const int32_t* blocks, int32_t n_blocks) {
+  if ((layout != MLA_LAYOUT_BLOCK_MAJOR && layout != MLA_LAYOUT_LAYER_MAJOR) || n_layers < 1 ||
+      page_bytes < 1 || pool_blocks < 1 || n_blocks < 0 || (n_blocks > 0 && !blocks))
+    return -1;
+  const int64_t n = (int64_t)n_blocks * n_layers;
+  if (n == 0) return 0;
+  int64_t* starts = (int64_t*)malloc(sizeof(int64_t) * n);
+  if (!starts) return -1;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    if (blocks[i] < 0 || blocks[i] >= pool_blocks) { free(starts); return -1; }
+    for (int32_t l = 0; l < n_layers; ++l) {
+      const int64_t page = layout == MLA_LAYOUT_BLOCK_MAJOR ? (int64_t)blocks[i] * n_layers + l
+                                                             : (int64_t)l * pool_blocks + blocks[i];
+      starts[(int64_t)i * n_layers + l] = page * page_bytes;
+    }
+  }
+  qsort(starts, (size_t)n, sizeof(int64_t), [](const void* x, const void* y) {
+    const int64_t a = *(const int64_t*)x, b = *(const int64_t*)y;
+    return (a > b) - (a < b);
+  });
+  int64_t regions = 0, end = -1;
+  for (int64_t k = 0; k < n; ++k) {
+    if (starts[k] != end) ++regions;        // a page that does not continue the previous range
+    end = starts[k] + page_bytes;
+  }
+  free(starts);
+  return regions;
 }
 
 mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,

@@ -61,4 +61,11 @@ hipError_t launch_stage_fp8(const void* cache, int64_t page_stride, int64_t cach
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream);
 
+// Pages of n_blocks blocks (all layers) from one multi-layer pool to another; layout 0 =
+// block-major, 1 = layer-major.
+hipError_t launch_copy_pages(const void* src, int64_t src_pool_blocks, void* dst,
+                             int64_t dst_pool_blocks, int32_t layout, int32_t n_layers,
+                             int64_t page_bytes, const int32_t* src_blocks,
+                             const int32_t* dst_blocks, int32_t n_blocks, hipStream_t stream);
+
 }  // namespace mla

@@ -166,3 +166,24 @@ def test_staged_workspace_size(lib):
     assert lib.mla_staged_workspace_size(T, H, k, 4) == rows + idx + bt + T * 4 * H * (512 * 2 + 4)
     # topk padded to whole 64-row pages
     assert lib.mla_staged_workspace_size(1, 16, 100, 1) == 128 * 576 + 512 + 256
+
+
+def test_kv_layout_entry_points(lib):
+    import numpy as np
+    from oracle import layout as lo
+    f = lib.mla_copy_kv_blocks
+    P = 22528
+    assert f(FAKE, 3 * P, FAKE, 3 * P, 0, 3, P, FAKE, FAKE, 0, None) == OK          # nothing to copy
+    assert f(FAKE, 3 * P, FAKE, 3 * P, 2, 3, P, FAKE, FAKE, 1, None) == INVALID     # layout
+    assert f(FAKE, 3 * P + 16, FAKE, 3 * P, 0, 3, P, FAKE, FAKE, 1, None) == INVALID  # not whole blocks
+    assert f(FAKE, 3 * P, FAKE, 3 * P, 0, 3, P + 8, FAKE, FAKE, 1, None) == INVALID  # page multiple of 16
+    assert f(None, 3 * P, FAKE, 3 * P, 0, 3, P, FAKE, FAKE, 1, None) == INVALID
+    # descriptor counts against the oracle's merged ranges
+    rng = np.random.default_rng(4)
+    for layout in (0, 1):
+        for blocks in ([5, 6, 7, 20], list(rng.choice(500, 60, replace=False)), list(range(100, 164))):
+            arr = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32))
+            n = lib.mla_kv_transfer_regions(layout, 7, P, 500, arr.ctypes.data_as(ctypes.c_void_p), arr.size)
+            assert n == len(lo.transfer_regions(layout, blocks, 7, P, 500))
+    bad = np.array([3, 500], dtype=np.int32)
+    assert lib.mla_kv_transfer_regions(0, 7, P, 500, bad.ctypes.data_as(ctypes.c_void_p), 2) == -1
