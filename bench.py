@@ -281,6 +281,31 @@ def counters_traffic(src_hash):
         return None
 
 
+# ---- top-k position selection ---------------------------------------------------------------------
+
+def topk_bench(dev, reps=20):
+    """Top-2048 positions per query token from fp32 scores (the step before the decode): the
+    pages' launch shape, the batched and the MTP shapes; graph-replayed launches."""
+    import torch
+    import nvfp4_compressed_mla_amd as m
+    res = {}
+    for name, B, q_len, n in (("pages_T15_146K", 1, 15, 149504), ("batched_T32_140K", 32, 1, 143360),
+                              ("mtp_T240_146K", 16, 15, 149504)):
+        g = torch.Generator(device=dev).manual_seed(77)
+        rot = 4
+        scores = [torch.randn(B, q_len, n, generator=g, device=dev) for _ in range(rot)]
+        seq = torch.full((B,), n, dtype=torch.int32, device=dev)
+        out = torch.empty(B, q_len, 2048, dtype=torch.int32, device=dev)
+        ws = torch.empty(m.mla_topk_workspace_size(B * q_len, n, 2048), dtype=torch.uint8, device=dev)
+        fn = lambda r: m.mla_topk_indices(scores[r % rot], seq, 2048, out=out, workspace=ws)
+        ms = time_steps(fn, rot, reps * rot, rot)
+        rd = B * q_len * n * 4
+        res[name] = {"us_per_launch": round(ms * 1e3, 2), "scores_read_GBps": round(rd / (ms * 1e-3) / 1e9, 1)}
+        del scores
+        torch.cuda.empty_cache()
+    return res
+
+
 # ---- block transfer between multi-layer pools --------------------------------------------------
 
 def kv_transfer(dev, n_layers=64, ctx=204800, pool_blocks=16000, reps=5):
@@ -400,7 +425,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way, kv_transfer (default all; 'none' = --no-extra)")
+                         "mixed, three_way, kv_transfer, topk (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -492,7 +517,7 @@ def main():
     }
 
     wanted = set() if args.no_extra or args.extras == "none" else (
-        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "kv_transfer"} if args.extras == "all"
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "kv_transfer", "topk"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
         extra = {}
@@ -551,6 +576,8 @@ def main():
                     del w2
                     torch.cuda.empty_cache()
                 extra[f"three_way_{shape}"] = cmp
+        if "topk" in wanted:
+            extra["topk_2048"] = topk_bench(dev)
         if "kv_transfer" in wanted:
             extra["kv_transfer_200K"] = kv_transfer(dev)
         result["extra"] = extra

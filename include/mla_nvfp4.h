@@ -224,6 +224,26 @@ mla_status mla_copy_kv_blocks(const void* src_pool, int64_t src_pool_bytes,
 int64_t mla_kv_transfer_regions(mla_kv_layout layout, int32_t n_layers, int64_t page_bytes,
                                 int64_t pool_blocks, const int32_t* blocks, int32_t n_blocks);
 
+/* ---- Top-k position selection (the indexer step before the path) ------------------------------
+ * Page section "Native NVFP4 sparse MLA decode kernel": the sparse indexer picks, for each query
+ * token, the positions attention reads (2048 per token); unused list entries are -1. The page
+ * does not define the indexer's scores; they are an input here.
+ *   scores   fp32 [B, q_len, n_max] device array: score of every position for every query token.
+ *   seq_lens int32 [B] device array; token t of request b may pick positions
+ *            0 .. seq_lens[b] - q_len + t (clamped to [0, n_max)).
+ *   out_idx  int32 [B, q_len, k]: the k positions with the largest scores, in ascending order,
+ *            then -1 when fewer than k positions are visible. Scores are ordered by the IEEE-754
+ *            total order of the float32 value (-0 below +0), equal scores by position (smaller
+ *            first); they must be finite. 1 <= k <= 2048, 1 <= n_max <= 212,992.
+ *   workspace mla_topk_workspace_size(B*q_len, n_max, k) bytes, 256-byte aligned (candidate
+ *            lists of 16,384-position chunks).
+ * The result is exact and deterministic: the same list for the same scores. */
+size_t mla_topk_workspace_size(int32_t num_tokens, int64_t n_max, int32_t k);
+
+mla_status mla_topk_indices(const float* scores, int64_t n_max, const int32_t* seq_lens,
+                            int32_t B, int32_t q_len, int32_t k, int32_t* out_idx,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Test hook, off the hot path: decode the rows at `slots` (int64 [n]) into fp32 [n, 576]
  * (latent then rope), through the same on-chip decoder the attention kernels use. Values are
  * exact. Slots outside the cache produce zeros. */

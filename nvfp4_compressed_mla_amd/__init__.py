@@ -10,19 +10,21 @@ from ._lib import (  # noqa: F401
     MlaError,
     load_library,
     mla_copy_kv_blocks,
-    mla_kv_transfer_regions,
     mla_decode_workspace_size,
     mla_dense_decode,
     mla_dense_decode_num_splits,
     mla_fp8_append,
     mla_fp8_dense_decode,
     mla_fp8_sparse_decode,
-    mla_nvfp4_stage_fp8,
-    mla_staged_sparse_decode,
-    mla_staged_workspace_size,
+    mla_kv_transfer_regions,
     mla_nvfp4_dequantize_rows,
     mla_nvfp4_quantize_append,
+    mla_nvfp4_stage_fp8,
     mla_set_timing_events,
     mla_sparse_decode,
     mla_sparse_decode_num_splits,
+    mla_staged_sparse_decode,
+    mla_staged_workspace_size,
+    mla_topk_indices,
+    mla_topk_workspace_size,
 )

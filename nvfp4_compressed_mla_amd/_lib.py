@@ -38,6 +38,8 @@ EXPORTED = [
     "mla_staged_sparse_decode",
     "mla_copy_kv_blocks",
     "mla_kv_transfer_regions",
+    "mla_topk_workspace_size",
+    "mla_topk_indices",
     "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
@@ -101,6 +103,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_copy_kv_blocks.restype = ctypes.c_int
     lib.mla_kv_transfer_regions.argtypes = [ctypes.c_int, i32, i64, i64, vp, i32]
     lib.mla_kv_transfer_regions.restype = i64
+    lib.mla_topk_workspace_size.argtypes = [i32, i64, i32]
+    lib.mla_topk_workspace_size.restype = sz
+    lib.mla_topk_indices.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.mla_topk_indices.restype = ctypes.c_int
     lib.mla_set_timing_events.argtypes = [vp, vp]
     lib.mla_set_timing_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -412,6 +418,32 @@ def mla_kv_transfer_regions(layout: int, n_layers: int, page_bytes: int, pool_bl
     if n < 0:
         raise MlaError(MLA_ERR_INVALID_ARG, "invalid layout arguments or block id outside the pool")
     return n
+
+
+def mla_topk_workspace_size(num_tokens: int, n_max: int, k: int) -> int:
+    return int(load_library().mla_topk_workspace_size(num_tokens, n_max, k))
+
+
+def mla_topk_indices(scores, seq_lens, k: int, out=None, workspace=None, stream=None):
+    """Top-k positions per query token from fp32 scores [B, q_len, n_max]; returns int32
+    [B, q_len, k] (ascending positions, -1 padded)."""
+    torch = _torch()
+    _require(scores, "scores", torch.float32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    if scores.dim() != 3 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous fp32 [B, q_len, n_max]")
+    B, q_len, n_max = scores.shape
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    if out is None:
+        out = torch.empty(B, q_len, k, dtype=torch.int32, device=scores.device)
+    need = mla_topk_workspace_size(B * q_len, n_max, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=scores.device)
+    _check(load_library().mla_topk_indices(
+        _ptr(scores), n_max, _ptr(seq_lens), B, q_len, int(k), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out
 
 
 def mla_set_timing_events(start, stop) -> None:

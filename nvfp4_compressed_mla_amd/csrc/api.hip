@@ -496,6 +496,32 @@ int64_t mla_kv_transfer_regions(mla_kv_layout layout, int32_t n_layers, int64_t 
   return regions;
 }
 
+size_t mla_topk_workspace_size(int32_t num_tokens, int64_t n_max, int32_t k) {
+  if (num_tokens < 1 || n_max < 1 || k < 1) return 0;
+  return mla::topk_ws_bytes(num_tokens, n_max, k);
+}
+
+mla_status mla_topk_indices(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t B,
+                            int32_t q_len, int32_t k, int32_t* out_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !seq_lens || !out_idx) return fail(MLA_ERR_INVALID_ARG, "null scores / seq_lens / out_idx");
+  if (B < 1 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B and q_len must be >= 1");
+  if (k < 1 || k > mla::kTopkMaxK) return fail(MLA_ERR_UNSUPPORTED, "k %d outside [1, %d]", k, mla::kTopkMaxK);
+  if (n_max < 1 || n_max > (int64_t)mla::kTopkChunk * mla::kTopkMaxChunks)
+    return fail(MLA_ERR_UNSUPPORTED, "n_max %lld outside [1, %d]", (long long)n_max,
+                mla::kTopkChunk * mla::kTopkMaxChunks);
+  const int64_t T = (int64_t)B * q_len;
+  if (T > (int64_t)1 << 20) return fail(MLA_ERR_INVALID_ARG, "too many query tokens");
+  if (!aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(out_idx, 4))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned scores / seq_lens / out_idx");
+  const size_t need = mla::topk_ws_bytes(T, n_max, k);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed", need);
+  return hip_status(mla::launch_topk(scores, n_max, seq_lens, (int32_t)T, q_len, k, workspace,
+                                     out_idx, stream),
+                    "topk launch");
+}
+
 mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,
                                      int64_t cache_bytes, const int64_t* slots, int64_t n,
                                      float* out, hipStream_t stream) {

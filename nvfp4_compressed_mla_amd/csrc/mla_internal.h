@@ -68,4 +68,16 @@ hipError_t launch_copy_pages(const void* src, int64_t src_pool_blocks, void* dst
                              int64_t page_bytes, const int32_t* src_blocks,
                              const int32_t* dst_blocks, int32_t n_blocks, hipStream_t stream);
 
+// Top-k position selection (scores fp32 [T, n_max], T = B*q_len): chunks of kTopkChunk positions,
+// at most kTopkMaxChunks of them, k <= kTopkMaxK.
+constexpr int kTopkChunk = 16384;
+constexpr int kTopkMaxChunks = 13;
+constexpr int kTopkMaxK = 2048;
+inline size_t topk_ws_bytes(int64_t T, int64_t n_max, int64_t k) {
+  const int64_t c = (n_max + kTopkChunk - 1) / kTopkChunk;
+  return (size_t)(T * c * k * 8 + T * c * 4);
+}
+hipError_t launch_topk(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t T,
+                       int32_t q_len, int32_t k, void* workspace, int32_t* out, hipStream_t stream);
+
 }  // namespace mla

@@ -187,3 +187,21 @@ def test_kv_layout_entry_points(lib):
             assert n == len(lo.transfer_regions(layout, blocks, 7, P, 500))
     bad = np.array([3, 500], dtype=np.int32)
     assert lib.mla_kv_transfer_regions(0, 7, P, 500, bad.ctypes.data_as(ctypes.c_void_p), 2) == -1
+
+
+def test_topk_entry_point_rejects(lib):
+    f = lib.mla_topk_indices
+    ws = lib.mla_topk_workspace_size(4, 1000, 64)
+    assert ws == 4 * 1 * 64 * 8 + 4 * 1 * 4
+    assert lib.mla_topk_workspace_size(15, 149504, 2048) == 15 * 10 * 2048 * 8 + 15 * 10 * 4
+    args = dict(s=FAKE, n=1000, sl=FAKE, B=2, q=2, k=64, o=FAKE, ws=FAKE, wb=1 << 20)
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return f(a["s"], a["n"], a["sl"], a["B"], a["q"], a["k"], a["o"], a["ws"], a["wb"], None)
+    assert call(s=None) == INVALID
+    assert call(k=0) == UNSUPPORTED
+    assert call(k=2049) == UNSUPPORTED
+    assert call(n=212993) == UNSUPPORTED
+    assert call(B=0) == INVALID
+    assert call(wb=100) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE

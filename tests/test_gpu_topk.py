@@ -1,0 +1,88 @@
+"""GPU top-k position selection: bit-exact against the oracle (positions are integers), with
+ties, signed zeros, causal windows, short contexts (-1 padding), chunk boundaries, the pages'
+launch shape at full size, and the selected lists feeding the sparse decode."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import topk as tk
+from tests import helpers as th
+
+pytestmark = pytest.mark.gpu
+
+
+def _m():
+    import nvfp4_compressed_mla_amd as m
+    return m
+
+
+def _run(scores, seq_lens, q_len, k):
+    m = _m()
+    s = torch.from_numpy(np.ascontiguousarray(scores)).cuda()
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    out = m.mla_topk_indices(s, sl, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.int64)
+
+
+@pytest.mark.parametrize("n_max,k,q_len,seq_lens,ties", [
+    (5000, 256, 1, [5000, 3000, 100], False),
+    (40000, 2048, 3, [40000, 17000], True),        # three chunks, causal window per token
+    (16384, 2048, 2, [16385, 2049], True),         # exactly one chunk; a window of 2048 - 1 + t
+    (33000, 512, 1, [33000], True),
+    (700, 2048, 1, [700], False),                  # fewer positions than k: -1 padding
+])
+def test_topk_matches_oracle(n_max, k, q_len, seq_lens, ties):
+    print(f"case: topk n_max={n_max} k={k} q_len={q_len} seq_lens={seq_lens} ties={ties}", flush=True)
+    rng = np.random.default_rng(n_max + k)
+    B = len(seq_lens)
+    s = rng.standard_normal((B, q_len, n_max)).astype(np.float32)
+    if ties:
+        s = np.round(s * 4) / 4                       # few distinct values: ties at the threshold
+        s[..., ::7] = -0.0
+        s[..., 3::11] = 0.0
+    got = _run(s, seq_lens, q_len, k)
+    want = tk.topk_indices(s, seq_lens, q_len, k)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    assert np.array_equal(_run(s, seq_lens, q_len, k), got)     # deterministic
+
+
+def test_topk_all_equal_and_signed_zeros():
+    print("case: topk all-equal scores and signed zeros", flush=True)
+    s = np.zeros((1, 2, 40000), dtype=np.float32)
+    s[0, 0] = 1.5
+    s[0, 1, ::2] = -0.0
+    got = _run(s, [40000], 2, 1000)
+    assert list(got[0, 0]) == list(range(1000))                 # ties by position
+    assert list(got[0, 1]) == list(range(1, 2000, 2))           # +0 above -0
+    assert np.array_equal(got, tk.topk_indices(s, [40000], 2, 1000))
+
+
+def test_topk_pages_shape_full_size():
+    """15 query tokens of one 149,504-token request, k = 2048 (the pages' launch shape)."""
+    print("case: topk pages shape 15 x 149504, k=2048", flush=True)
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((1, 15, 149504)).astype(np.float32)
+    got = _run(s, [149504], 15, 2048)
+    want = tk.topk_indices(s, [149504], 15, 2048)
+    assert np.array_equal(got, want)
+
+
+def test_topk_feeds_sparse_decode():
+    print("case: topk -> sparse decode", flush=True)
+    m = _m()
+    case = th.build_case(2, 2, 64, [3000, 2100], 0, seed=55)
+    rng = np.random.default_rng(56)
+    n_max = 3000
+    s = rng.standard_normal((2, 2, n_max)).astype(np.float32)
+    idx = m.mla_topk_indices(torch.from_numpy(s).cuda(), case.seq_lens, 700)
+    case.topk_idx = idx
+    case.topk = 700
+    out, lse = m.mla_sparse_decode(case.q, case.cache, case.page_stride, case.block_table, idx,
+                                   th.softmax_scale())
+    torch.cuda.synchronize()
+    want_idx = tk.topk_indices(s, [3000, 2100], 2, 700)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    ref_o, ref_l = th.oracle_sparse(case)
+    th.assert_parity(out, lse, ref_o, ref_l, what="topk -> decode")
