@@ -61,20 +61,22 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& a_ex, int& b_ex, 
   __syncthreads();                                         // wsum is reused by the next call
 }
 
-constexpr int kTopkSubHists = kTopkThreads / 16;           // one histogram per 16 lanes
+constexpr int kHistStride = 257;                          // padded: lanes hit different banks
 
 // k-th largest of keys[0:m) (1 <= k <= m): returns the threshold key and, through `need`, how many
 // keys equal to it belong to the top k (all keys above it do). Scores cluster in few values of
-// the leading digit, so each 16-lane group counts into a histogram of its own (LDS atomics on
-// one address serialize), and the 32 are summed before the digit is chosen.
-__device__ uint32_t radix_select(const uint32_t* keys, int m, int k, uint32_t* hist /* LDS 32 x 256 */,
+// the leading digit and LDS atomics on one address serialize, so lane l of every wave counts into
+// histogram l % NSUB (rows padded to 257 words, so that one bin of different histograms falls in
+// different banks); the NSUB histograms are summed before the digit is chosen.
+template <int NSUB>
+__device__ uint32_t radix_select(const uint32_t* keys, int m, int k, uint32_t* hist /* LDS NSUB x 257 */,
                                  int* state /* LDS 2 */, int& need) {
   uint32_t prefix = 0, mask = 0;
   int rem = k;
   const int tid = threadIdx.x, lane = tid & 63;
-  uint32_t* my_hist = hist + (tid >> 4) * 256;
+  uint32_t* my_hist = hist + (lane % NSUB) * kHistStride;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kTopkSubHists * 256; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < NSUB * kHistStride; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int p0 = tid; p0 < m; p0 += 8 * kTopkThreads) {   // 8 LDS reads in flight per lane
       uint32_t kk[8];
@@ -89,12 +91,13 @@ __device__ uint32_t radix_select(const uint32_t* keys, int m, int k, uint32_t* h
           atomicAdd(&my_hist[(kk[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
+    uint32_t tot = 0;
     if (tid < 256) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int h = 0; h < kTopkSubHists; ++h) t += hist[h * 256 + tid];
-      hist[tid] = t;                                       // sub-histogram 0 now holds the sums
+#pragma unroll 16
+      for (int h = 0; h < NSUB; ++h) tot += hist[h * kHistStride + tid];
     }
+    __syncthreads();
+    if (tid < 256) hist[tid] = tot;                        // histogram 0 now holds the sums
     __syncthreads();
     if (tid < 64) {
       // lane l holds bins 255-4l .. 252-4l (descending); counts above a lane's bins by a scan
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(
     int32_t q_len, int32_t k, int32_t n_chunks, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_pos, int32_t* __restrict__ cand_cnt) {
   __shared__ uint32_t keys[kTopkChunk];
-  __shared__ uint32_t hist[kTopkSubHists * 256];
+  __shared__ uint32_t hist[64 * kHistStride];
   __shared__ int state[2];
   __shared__ int wsum[16];
   const int tok = blockIdx.x / n_chunks, c = blockIdx.x - tok * n_chunks;
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(
   }
   __syncthreads();
   int need = k;                                            // m <= k: keep everything
-  const uint32_t thr = (m > k) ? radix_select(keys, m, k, hist, state, need) : 0u;   // 0: below every finite key
+  const uint32_t thr = (m > k) ? radix_select<64>(keys, m, k, hist, state, need) : 0u;   // 0: below every finite key
   ordered_emit(keys, m, thr, need, wsum, [&](int p) { return c0 + p; },
                [&](int slot, int p, int32_t pos) {
                  cand_key[cbase + slot] = keys[p];
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     int32_t n_chunks, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
     const int32_t* __restrict__ cand_cnt, int32_t* __restrict__ out) {
   __shared__ uint32_t keys[kTopkMaxChunks * kTopkMaxK];
-  __shared__ uint32_t hist[kTopkSubHists * 256];
+  __shared__ uint32_t hist[16 * kHistStride];
   __shared__ int state[2];
   __shared__ int wsum[16];
   __shared__ int coff[kTopkMaxChunks + 1];
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   }
   __syncthreads();
   int need = k;
-  const uint32_t thr = (total > k) ? radix_select(keys, total, k, hist, state, need) : 0u;
+  const uint32_t thr = (total > k) ? radix_select<16>(keys, total, k, hist, state, need) : 0u;
   int32_t* orow = out + (int64_t)tok * k;
   int c = 0;                                               // chunk of the last candidate seen
   ordered_emit(keys, total, thr, need, wsum,
