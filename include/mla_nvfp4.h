@@ -234,9 +234,9 @@ int64_t mla_kv_transfer_regions(mla_kv_layout layout, int32_t n_layers, int64_t 
  *   out_idx  int32 [B, q_len, k]: the k positions with the largest scores, in ascending order,
  *            then -1 when fewer than k positions are visible. Scores are ordered by the IEEE-754
  *            total order of the float32 value (-0 below +0), equal scores by position (smaller
- *            first); they must be finite. 1 <= k <= 2048, 1 <= n_max <= 212,992.
+ *            first); they must be finite. 1 <= k <= 2048, 1 <= n_max <= 1,048,576.
  *   workspace mla_topk_workspace_size(B*q_len, n_max, k) bytes, 256-byte aligned (candidate
- *            lists of 16,384-position chunks).
+ *            lists of the position segments, about 256 KiB per token at most).
  * The result is exact and deterministic: the same list for the same scores. */
 size_t mla_topk_workspace_size(int32_t num_tokens, int64_t n_max, int32_t k);
 

@@ -507,9 +507,9 @@ mla_status mla_topk_indices(const float* scores, int64_t n_max, const int32_t* s
   if (!scores || !seq_lens || !out_idx) return fail(MLA_ERR_INVALID_ARG, "null scores / seq_lens / out_idx");
   if (B < 1 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B and q_len must be >= 1");
   if (k < 1 || k > mla::kTopkMaxK) return fail(MLA_ERR_UNSUPPORTED, "k %d outside [1, %d]", k, mla::kTopkMaxK);
-  if (n_max < 1 || n_max > (int64_t)mla::kTopkChunk * mla::kTopkMaxChunks)
-    return fail(MLA_ERR_UNSUPPORTED, "n_max %lld outside [1, %d]", (long long)n_max,
-                mla::kTopkChunk * mla::kTopkMaxChunks);
+  if (n_max < 1 || n_max > mla::kTopkMaxN)
+    return fail(MLA_ERR_UNSUPPORTED, "n_max %lld outside [1, %lld]", (long long)n_max,
+                (long long)mla::kTopkMaxN);
   const int64_t T = (int64_t)B * q_len;
   if (T > (int64_t)1 << 20) return fail(MLA_ERR_INVALID_ARG, "too many query tokens");
   if (!aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(out_idx, 4))

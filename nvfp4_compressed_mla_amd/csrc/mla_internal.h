@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace mla {
 
 // Arguments of the fused decode kernel (one struct, passed by value).
@@ -68,14 +70,33 @@ hipError_t launch_copy_pages(const void* src, int64_t src_pool_blocks, void* dst
                              int64_t page_bytes, const int32_t* src_blocks,
                              const int32_t* dst_blocks, int32_t n_blocks, hipStream_t stream);
 
-// Top-k position selection (scores fp32 [T, n_max], T = B*q_len): chunks of kTopkChunk positions,
-// at most kTopkMaxChunks of them, k <= kTopkMaxK.
-constexpr int kTopkChunk = 16384;
-constexpr int kTopkMaxChunks = 13;
+// Top-k position selection (scores fp32 [T, n_max], T = B*q_len, k <= kTopkMaxK). A token's
+// positions are cut into n_slices slices of `slice` positions (one filter workgroup each, eight
+// wave segments of slice / 8); each segment lists at most cap_seg candidates.
 constexpr int kTopkMaxK = 2048;
-inline size_t topk_ws_bytes(int64_t T, int64_t n_max, int64_t k) {
-  const int64_t c = (n_max + kTopkChunk - 1) / kTopkChunk;
-  return (size_t)(T * c * k * 8 + T * c * 4);
+constexpr int64_t kTopkMaxN = 1 << 20;
+constexpr int kTopkTakeAll = 8192;            // rows this short are selected directly in LDS
+constexpr int kTopkCandCap = 8192;            // candidates the merge holds in LDS
+constexpr int kTopkSample = 2048;             // sample size of the cut
+constexpr int kTopkMaxSlices = 16;
+struct TopkPlan {
+  int64_t slice;
+  int32_t n_slices;
+  int32_t cap_seg;
+};
+inline TopkPlan topk_plan(int64_t T, int64_t n_max) {
+  // at most 512 filter workgroups (two per compute unit: one round), at most 16 per token
+  const int64_t g = std::min<int64_t>(kTopkMaxSlices, std::max<int64_t>(1, 512 / T));
+  TopkPlan p;
+  p.slice = (((n_max + g - 1) / g) + 2047) / 2048 * 2048;
+  p.n_slices = (int32_t)((n_max + p.slice - 1) / p.slice);
+  p.cap_seg = (int32_t)std::min<int64_t>(p.slice / 8, std::min<int64_t>(4096, std::max<int64_t>(256, 32768 / (8 * p.n_slices))));
+  return p;
+}
+inline size_t topk_ws_bytes(int64_t T, int64_t n_max, int64_t /*k*/) {
+  const TopkPlan p = topk_plan(T, n_max);
+  const int64_t segs = T * p.n_slices * 8;
+  return (size_t)(segs * p.cap_seg * 8 + segs * 4);
 }
 hipError_t launch_topk(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t T,
                        int32_t q_len, int32_t k, void* workspace, int32_t* out, hipStream_t stream);

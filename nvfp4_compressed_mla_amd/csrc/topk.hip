@@ -7,15 +7,25 @@
 // kept, scores ordered by the IEEE-754 total order of their float32 value (-0 below +0) and equal
 // scores by position (smaller first); the list holds them in ascending position order, then -1.
 //
-// Two launches, both exact:
-//  1. topk_chunk_kernel: one workgroup per (token, 16384-position chunk) loads the chunk's keys
-//     (order-preserving uint32 images of the scores) into LDS, finds the chunk's k-th largest key
-//     by a 4 x 8-bit radix select (LDS histograms), and writes the chunk's top k (key, position)
-//     in position order. The token's top k is contained in the union of its chunks' top k.
-//  2. topk_merge_kernel: one workgroup per token selects the top k of that union the same way
-//     and writes the positions in ascending order, padded with -1.
-// Both emit in position order with a block-wide scan of (greater, equal-to-threshold) counts, so
-// the result is deterministic.
+// Two launches, both exact (every score is compared as an order-preserving uint32 key):
+//  1. topk_filter_kernel, one workgroup per (token, slice of positions). Every workgroup of a
+//     token draws the same sample of 2048 scores (256 evenly spaced runs of 8) and takes the
+//     sample's r-th largest key, low 8 bits cleared, as a cut L, r chosen so that the number of
+//     positions with a key >= L lies between k and the merge's capacity with overwhelming
+//     probability. Each wave then streams its contiguous segment of the slice and appends the
+//     positions with key >= L, in position order, to the segment's list (ballot + mbcnt; no
+//     atomics, no histogram over the whole row).
+//  2. topk_merge_kernel, one workgroup per token. If every list fitted and the lists hold between
+//     k and 8192 entries, they contain the exact top k (every other key is below L, and L is at
+//     most the k-th largest candidate), so the k-th largest candidate is found by a radix select
+//     in LDS (12-bit digits of the key's offset from the smallest candidate) and the positions
+//     are written in ascending order. Otherwise (a sample that missed, heavy ties) the workgroup selects from the
+//     token's full row itself: the same radix select and ordered emission, reading the scores
+//     from memory; slow, but exact. Tokens with at most 8192 visible positions are selected
+//     directly from their row in LDS.
+// The emission ranks every entry by wave ballots and a scan of the per-wave counts of (greater,
+// equal-to-threshold) entries, so the result is deterministic. Wave-level scans and reductions use
+// DPP row shifts and row broadcasts (no LDS round trip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,8 +34,12 @@
 namespace mla {
 
 constexpr int kTopkThreads = 512;
-constexpr int kTopkPerThread = 8;                          // positions per thread per emit round
-constexpr int kTopkRound = kTopkThreads * kTopkPerThread;  // 4096
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkPerThread = 16;                         // entries per thread per emit round
+constexpr int kTopkRound = kTopkThreads * kTopkPerThread;  // 8192: one round for LDS lists
+constexpr int kTopkSampleRuns = kTopkSample / 8;           // runs of 8 consecutive positions
+constexpr int kFilterUnroll = 32;                          // loads in flight per lane
+constexpr int kBins = 4096;                                // 12-bit digits
 
 // Order-preserving image of a float: a > b (IEEE total order) <=> key(a) > key(b).
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -33,138 +47,190 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive scan of two counters (512 threads = 8 waves); also returns the totals.
-__device__ __forceinline__ void block_scan2(int a, int b, int& a_ex, int& b_ex, int& a_tot, int& b_tot,
-                                            int* wsum /* LDS [2][8] */) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int ta = __shfl_up(ia, d), tb = __shfl_up(ib, d);
-    if (lane >= d) { ia += ta; ib += tb; }
-  }
-  if (lane == 63) { wsum[wv] = ia; wsum[8 + wv] = ib; }
-  __syncthreads();
-  int pa = 0, pb = 0, ta = 0, tb = 0;
-#pragma unroll
-  for (int v = 0; v < kTopkThreads / 64; ++v) {
-    const int sa = wsum[v], sb = wsum[8 + v];
-    pa += (v < wv) ? sa : 0;
-    pb += (v < wv) ? sb : 0;
-    ta += sa;
-    tb += sb;
-  }
-  a_ex = pa + ia - a;
-  b_ex = pb + ib - b;
-  a_tot = ta;
-  b_tot = tb;
-  __syncthreads();                                         // wsum is reused by the next call
+// x moved by a DPP pattern; lanes without a source (or in rows outside ROW_MASK) get `fill`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t fill, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, CTRL, ROW_MASK, 0xF, false);
 }
 
-constexpr int kHistStride = 257;                          // padded: lanes hit different banks
+// Inclusive scan of the 64 lanes of a wave under `op`, `id` its identity: shifts by 1, 2, 4 and
+// 8 lanes inside each row of 16, then the last lane of row 0 (2) into row 1 (3), and of row 1
+// into rows 2 and 3.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_move<0x111, 0xF>(id, x));                // row_shr:1
+  x = op(x, dpp_move<0x112, 0xF>(id, x));                // row_shr:2
+  x = op(x, dpp_move<0x114, 0xF>(id, x));                // row_shr:4
+  x = op(x, dpp_move<0x118, 0xF>(id, x));                // row_shr:8
+  x = op(x, dpp_move<0x142, 0xA>(id, x));                // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_move<0x143, 0xC>(id, x));                // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  return (int)wave_scan((uint32_t)x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
 
-// k-th largest of keys[0:m) (1 <= k <= m): returns the threshold key and, through `need`, how many
-// keys equal to it belong to the top k (all keys above it do). Scores cluster in few values of
-// the leading digit and LDS atomics on one address serialize, so lane l of every wave counts into
-// histogram l % NSUB (rows padded to 257 words, so that one bin of different histograms falls in
-// different banks); the NSUB histograms are summed before the digit is chosen.
-template <int NSUB>
-__device__ uint32_t radix_select(const uint32_t* keys, int m, int k, uint32_t* hist /* LDS NSUB x 257 */,
-                                 int* state /* LDS 2 */, int& need) {
-  uint32_t prefix = 0, mask = 0;
+// Block-wide exclusive sum over the 512 threads (also the total). No barrier at the end: the
+// caller passes one before wsum is written again.
+__device__ __forceinline__ int block_excl_sum(int a, int& tot, int* wsum /* LDS 8 */) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ia = wave_incl_sum(a);
+  if (lane == 63) wsum[wv] = ia;
+  __syncthreads();
+  int pa = 0, ta = 0;
+#pragma unroll
+  for (int v = 0; v < kTopkWaves; ++v) {
+    const int sa = wsum[v];
+    pa += (v < wv) ? sa : 0;
+    ta += sa;
+  }
+  tot = ta;
+  return pa + ia - a;
+}
+
+// Smallest and largest of key_at(0 .. m-1) (m >= 1), the same in every thread.
+template <typename KeyAt>
+__device__ void block_minmax(KeyAt key_at, int m, uint32_t& mn, uint32_t& mx, uint32_t* red /* LDS 16 */) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+  for (int p = threadIdx.x; p < m; p += kTopkThreads) {
+    const uint32_t v = key_at(p);
+    a = min(a, v);
+    b = max(b, v);
+  }
+  a = wave_scan(a, 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return min(x, y); });
+  b = wave_scan(b, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (lane == 63) { red[wv] = a; red[kTopkWaves + wv] = b; }
+  __syncthreads();
+  mn = red[0];
+  mx = red[kTopkWaves];
+#pragma unroll
+  for (int v = 1; v < kTopkWaves; ++v) { mn = min(mn, red[v]); mx = max(mx, red[kTopkWaves + v]); }
+}
+
+// k-th largest of key_at(0 .. m-1) (1 <= k <= m), all keys >= base and key - base < 2^(hi+1).
+// The offsets d = key - base (same order as the keys) are resolved as radix digits of up to 12
+// bits from bit hi down, at most `max_passes` of them (fewer passes leave the unresolved low bits
+// zero: a lower bound of the k-th largest). Returns the threshold and, through `need`, how many
+// keys equal to it belong to the top k (all keys above it do). Each pass counts the offsets that
+// match the resolved prefix into a 4096-bin LDS histogram (two buffers: the next one is cleared
+// while this one fills); thread t owns bins 4095 - 8t .. 4088 - 8t, so a block scan of its 8-bin
+// sums gives the number of keys above them.
+template <typename KeyAt>
+__device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi, int max_passes,
+                               uint32_t* hist /* LDS 2 x 4096 */, int* wsum, int* state, int& need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = (hi >= 31) ? 0u : ~((2u << hi) - 1u);
   int rem = k;
-  const int tid = threadIdx.x, lane = tid & 63;
-  uint32_t* my_hist = hist + (lane % NSUB) * kHistStride;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < NSUB * kHistStride; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    for (int p0 = tid; p0 < m; p0 += 8 * kTopkThreads) {   // 8 LDS reads in flight per lane
-      uint32_t kk[8];
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  __syncthreads();
+  for (int pass = 0; hi >= 0 && pass < max_passes; ++pass) {
+    const int shift = max(hi - 11, 0);
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;
+    uint32_t* h = hist + (pass & 1) * kBins;
+    uint32_t* h_next = hist + ((pass + 1) & 1) * kBins;
+    for (int p0 = tid; p0 < m; p0 += 8 * kTopkThreads) {   // 8 reads in flight per lane
+      uint32_t dd[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int p = p0 + j * kTopkThreads;
-        kk[j] = (p < m) ? keys[p] : 0u;
+        dd[j] = (p < m) ? key_at(p) - base : 0u;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (p0 + j * kTopkThreads < m && (kk[j] & mask) == prefix)
-          atomicAdd(&my_hist[(kk[j] >> shift) & 255u], 1u);
+        if (p0 + j * kTopkThreads < m && (dd[j] & mask) == prefix) atomicAdd(&h[(dd[j] >> shift) & dmask], 1u);
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) h_next[i] = 0;
+    __syncthreads();
+    int c[8], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { c[j] = (int)h[kBins - 1 - 8 * tid - j]; sum += c[j]; }
+    int tot;
+    int run = block_excl_sum(sum, tot, wsum);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (run < rem && run + c[j] >= rem) { state[0] = kBins - 1 - 8 * tid - j; state[1] = rem - run; }
+      run += c[j];
     }
     __syncthreads();
-    uint32_t tot = 0;
-    if (tid < 256) {
-#pragma unroll 16
-      for (int h = 0; h < NSUB; ++h) tot += hist[h * kHistStride + tid];
-    }
-    __syncthreads();
-    if (tid < 256) hist[tid] = tot;                        // histogram 0 now holds the sums
-    __syncthreads();
-    if (tid < 64) {
-      // lane l holds bins 255-4l .. 252-4l (descending); counts above a lane's bins by a scan
-      int c[4], s = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = (int)hist[255 - 4 * lane - j]; s += c[j]; }
-      int inc = s;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(inc, d);
-        if (lane >= d) inc += t;
-      }
-      int run = inc - s;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run < rem && run + c[j] >= rem) { state[0] = 255 - 4 * lane - j; state[1] = rem - run; }
-        run += c[j];
-      }
-    }
-    __syncthreads();
-    const int d = state[0];
+    prefix |= (uint32_t)state[0] << shift;
+    mask |= dmask << shift;
     rem = state[1];
-    prefix |= (uint32_t)d << shift;
-    mask |= 0xFFu << shift;
-    __syncthreads();
+    hi = shift - 1;
   }
   need = rem;
-  return prefix;
+  return base + prefix;
 }
 
-// Emit, in list order, the entries of keys[0:m) above thr plus the first `need` equal to it:
-// payload(i) is fetched for every entry of a thread's round up front (so that its loads overlap),
-// then emit(slot, payload) is called for the selected ones.
-template <typename Payload, typename Emit>
-__device__ void ordered_emit(const uint32_t* keys, int m, uint32_t thr, int need, int* wsum,
+// k-th largest of keys that sit in LDS (1 <= k <= m), on offsets from the smallest key.
+template <typename KeyAt>
+__device__ uint32_t select_kth_lds(KeyAt key_at, int m, int k, uint32_t* hist, int* wsum, int* state,
+                                   uint32_t* red, int& need) {
+  uint32_t mn, mx;
+  block_minmax(key_at, m, mn, mx, red);
+  if (mn == mx) { need = k; return mx; }
+  return select_kth(key_at, m, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
+}
+
+// Emit, in list order, the entries of key_at(0 .. m-1) above thr plus the first `need` equal to
+// it, as emit(slot, payload(i)). Rounds of 8192 entries: entry r0 + 512 j + tid is thread tid's
+// j-th, so an entry's rank is (counts of the waves' ballots of earlier (j, wave) pairs, scanned by
+// wave 0) + (its rank in its own ballot).
+template <typename KeyAt, typename Payload, typename Emit>
+__device__ void ordered_emit(KeyAt key_at, int m, uint32_t thr, int need, int* cnt /* LDS 514 */,
                              Payload payload, Emit emit) {
+  constexpr int kQ = kTopkPerThread * kTopkWaves;          // 128 (j, wave) pairs
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int gc = 0, ec = 0;                                     // carried over rounds
   for (int r0 = 0; r0 < m; r0 += kTopkRound) {
-    const int p0 = r0 + threadIdx.x * kTopkPerThread;
+    const int jn = min(kTopkPerThread, (m - r0 + kTopkThreads - 1) / kTopkThreads);   // rows present
     uint32_t kk[kTopkPerThread];
     int32_t pl[kTopkPerThread];
-    int g = 0, e = 0;
 #pragma unroll
     for (int j = 0; j < kTopkPerThread; ++j) {
-      const int p = p0 + j;
-      kk[j] = (p < m) ? keys[p] : 0u;
+      const int p = r0 + j * kTopkThreads + tid;
+      kk[j] = (p < m) ? key_at(p) : 0u;
       pl[j] = (p < m) ? payload(p) : 0;
-      g += (p < m && kk[j] > thr);
-      e += (p < m && kk[j] == thr);
     }
-    int g_ex, e_ex, g_tot, e_tot;
-    block_scan2(g, e, g_ex, e_ex, g_tot, e_tot, wsum);
-    int gb = gc + g_ex, eb = ec + e_ex;
 #pragma unroll
     for (int j = 0; j < kTopkPerThread; ++j) {
-      const int p = p0 + j;
-      if (p >= m) break;
-      if (kk[j] > thr) {
-        emit(gb + min(eb, need), p, pl[j]);
-        ++gb;
-      } else if (kk[j] == thr) {
-        if (eb < need) emit(gb + eb, p, pl[j]);
-        ++eb;
+      if (j >= jn) {                                       // workgroup-uniform
+        if (lane == 0) { cnt[j * kTopkWaves + w] = 0; cnt[kQ + j * kTopkWaves + w] = 0; }
+        continue;
       }
+      const bool in = r0 + j * kTopkThreads + tid < m;
+      const uint64_t bg = __ballot(in && kk[j] > thr), be = __ballot(in && kk[j] == thr);
+      if (lane == 0) { cnt[j * kTopkWaves + w] = __popcll(bg); cnt[kQ + j * kTopkWaves + w] = __popcll(be); }
     }
-    gc += g_tot;
-    ec += e_tot;
+    __syncthreads();
+    if (w == 0) {
+      // lane l: pairs 2l and 2l + 1, for both counters; exclusive offsets replace the counts
+      const int g0 = cnt[2 * lane], g1 = cnt[2 * lane + 1];
+      const int e0 = cnt[kQ + 2 * lane], e1 = cnt[kQ + 2 * lane + 1];
+      const int gi = wave_incl_sum(g0 + g1), ei = wave_incl_sum(e0 + e1);
+      cnt[2 * lane] = gi - g0 - g1;
+      cnt[2 * lane + 1] = gi - g1;
+      cnt[kQ + 2 * lane] = ei - e0 - e1;
+      cnt[kQ + 2 * lane + 1] = ei - e1;
+      if (lane == 63) { cnt[2 * kQ] = gi; cnt[2 * kQ + 1] = ei; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread; ++j) {
+      if (j >= jn) break;                                  // workgroup-uniform
+      const bool in = r0 + j * kTopkThreads + tid < m;
+      const bool gt = in && kk[j] > thr, eq = in && kk[j] == thr;
+      const uint64_t bg = __ballot(gt), be = __ballot(eq);
+      const int gb = gc + cnt[j * kTopkWaves + w] +
+                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+      const int eb = ec + cnt[kQ + j * kTopkWaves + w] +
+                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      if (gt) emit(gb + min(eb, need), pl[j]);
+      else if (eq && eb < need) emit(gb + eb, pl[j]);
+    }
+    gc += cnt[2 * kQ];
+    ec += cnt[2 * kQ + 1];
+    __syncthreads();                                       // cnt is written again next round
   }
 }
 
@@ -174,111 +240,213 @@ __device__ __forceinline__ int visible(const int32_t* seq_lens, int tok, int q_l
   return (int)(v < 0 ? 0 : (v > n_max ? n_max : v));
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(
+// Rank r of the cut in the sample (n > kTopkTakeAll). With e = k * 2048 / n sample entries
+// expected among the top k, r = 1.5 e + 3 sqrt(e) + 2 puts the number of positions at or above
+// the cut near 1.5 k + 3 sqrt(k n / 2048): above k, and below 8192 for k <= 2048, unless the
+// sample is more than about five standard deviations off.
+__device__ __forceinline__ int sample_rank(int k, int n) {
+  const float e = (float)k * (float)kTopkSample / (float)n;
+  const int r = (int)__builtin_ceilf(1.5f * e + 3.0f * __builtin_sqrtf(e)) + 2;
+  return min(max(r, 1), kTopkSample);
+}
+
+// Position of sample entry i: run i / 8 of 256 evenly spaced runs of 8 positions.
+__device__ __forceinline__ int sample_pos(int i, int n) {
+  return (int)(((int64_t)(i >> 3) * n) / kTopkSampleRuns) + (i & 7);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t n_max, const int32_t* __restrict__ seq_lens,
-    int32_t q_len, int32_t k, int32_t n_chunks, uint32_t* __restrict__ cand_key,
-    int32_t* __restrict__ cand_pos, int32_t* __restrict__ cand_cnt) {
-  __shared__ uint32_t keys[kTopkChunk];
-  __shared__ uint32_t hist[64 * kHistStride];
+    int32_t q_len, int32_t k, int64_t slice, int32_t n_slices, int32_t cap_seg,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_pos, int32_t* __restrict__ seg_cnt) {
+  __shared__ uint32_t skeys[kTopkSample];
+  __shared__ uint32_t hist[2 * kBins];
+  __shared__ int wsum[kTopkWaves];
   __shared__ int state[2];
-  __shared__ int wsum[16];
-  const int tok = blockIdx.x / n_chunks, c = blockIdx.x - tok * n_chunks;
+  const int tok = blockIdx.x / n_slices, g = blockIdx.x - tok * n_slices;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t seg = ((int64_t)tok * n_slices + g) * kTopkWaves + w;
+  const float* row = scores + (int64_t)tok * n_max;
+  // this wave's segment of the slice, in batches of kFilterUnroll rows of 64 positions; the
+  // first batch is loaded before the row length is known (bounded by the row's n_max entries)
+  // and stays in flight while the cut is found
+  const int64_t seg_len = slice / kTopkWaves;
+  const int64_t p_begin = (int64_t)g * slice + w * seg_len;
+  auto load_batch = [&](int64_t b0, int64_t lim, float (&v)[kFilterUnroll]) {
+#pragma unroll
+    for (int j = 0; j < kFilterUnroll; ++j) {
+      const int64_t p = b0 + j * 64 + lane;
+      v[j] = (p < lim) ? row[p] : 0.0f;
+    }
+  };
+  float cur[kFilterUnroll];
+  load_batch(p_begin, min(p_begin + seg_len, n_max), cur);
   const int n = visible(seq_lens, tok, q_len, n_max);
-  const int c0 = c * kTopkChunk;
-  const int m = max(0, min(n - c0, kTopkChunk));
-  const int64_t cbase = ((int64_t)tok * n_chunks + c) * k;
-  if (threadIdx.x == 0) cand_cnt[(int64_t)tok * n_chunks + c] = min(m, k);
-  if (m == 0) return;                                      // workgroup-uniform
-  const float* row = scores + (int64_t)tok * n_max + c0;
-  {
-    // every load of the chunk in flight at once (32 per thread), then the keys to LDS
-    constexpr int kPer = kTopkChunk / kTopkThreads;
-    float v[kPer];
+  if (n <= kTopkTakeAll || (int64_t)g * slice >= n) {     // workgroup-uniform
+    if (lane == 0) seg_cnt[seg] = 0;
+    return;
+  }
+  const int64_t p_end = min(p_begin + seg_len, (int64_t)n);
+  // the sample (identical in every workgroup of the token) and its cut: the top 24 bits of its
+  // r-th largest key
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = threadIdx.x + j * kTopkThreads;
-      v[j] = (p < m) ? row[p] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = threadIdx.x + j * kTopkThreads;
-      if (p < m) keys[p] = score_key(v[j]);
-    }
+  for (int j = 0; j < kTopkSample / kTopkThreads; ++j) {
+    const int i = threadIdx.x * (kTopkSample / kTopkThreads) + j;
+    skeys[i] = score_key(row[sample_pos(i, n)]);
   }
   __syncthreads();
-  int need = k;                                            // m <= k: keep everything
-  const uint32_t thr = (m > k) ? radix_select<64>(keys, m, k, hist, state, need) : 0u;   // 0: below every finite key
-  ordered_emit(keys, m, thr, need, wsum, [&](int p) { return c0 + p; },
-               [&](int slot, int p, int32_t pos) {
-                 cand_key[cbase + slot] = keys[p];
-                 cand_pos[cbase + slot] = pos;
-               });
+  int unused;
+  const uint32_t cut = select_kth([&](int i) { return skeys[i]; }, kTopkSample, sample_rank(k, n),
+                                  0u, 31, 2, hist, wsum, state, unused);
+  uint32_t* ck = cand_key + seg * cap_seg;
+  int32_t* cp = cand_pos + seg * cap_seg;
+  int cnt = 0;
+  for (int64_t b0 = p_begin; b0 < p_end; b0 += 64 * kFilterUnroll) {
+    float nxt[kFilterUnroll];
+    if (b0 + 64 * kFilterUnroll < p_end) load_batch(b0 + 64 * kFilterUnroll, p_end, nxt);   // next batch in flight
+#pragma unroll
+    for (int j = 0; j < kFilterUnroll; ++j) {
+      const int64_t p = b0 + j * 64 + lane;
+      const uint32_t key = score_key(cur[j]);
+      const bool sel = p < p_end && key >= cut;
+      const uint64_t mask = __ballot(sel);
+      if (sel) {
+        const int at = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (at < cap_seg) { ck[at] = key; cp[at] = (int32_t)p; }
+      }
+      cnt += __popcll(mask);
+    }
+#pragma unroll
+    for (int j = 0; j < kFilterUnroll; ++j) cur[j] = nxt[j];
+  }
+  if (lane == 0) seg_cnt[seg] = cnt;                       // the true count, even past cap_seg
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
-    int64_t n_max, const int32_t* __restrict__ seq_lens, int32_t q_len, int32_t k,
-    int32_t n_chunks, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-    const int32_t* __restrict__ cand_cnt, int32_t* __restrict__ out) {
-  __shared__ uint32_t keys[kTopkMaxChunks * kTopkMaxK];
-  __shared__ uint32_t hist[16 * kHistStride];
+    const float* __restrict__ scores, int64_t n_max, const int32_t* __restrict__ seq_lens,
+    int32_t q_len, int32_t k, int32_t n_slices, int32_t cap_seg,
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
+    const int32_t* __restrict__ seg_cnt, int32_t* __restrict__ out) {
+  __shared__ uint32_t keys[kTopkCandCap];
+  __shared__ int32_t pos[kTopkCandCap];
+  __shared__ uint32_t hist[2 * kBins];
   __shared__ int state[2];
-  __shared__ int wsum[16];
-  __shared__ int coff[kTopkMaxChunks + 1];
-  const int tok = blockIdx.x;
-  const int64_t tbase = (int64_t)tok * n_chunks;
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int c = 0; c < n_chunks; ++c) { coff[c] = o; o += cand_cnt[tbase + c]; }
-    coff[n_chunks] = o;
+  __shared__ int wsum[kTopkWaves];
+  __shared__ uint32_t red[2 * kTopkWaves];
+  __shared__ int cnt[2 * kTopkPerThread * kTopkWaves + 2];
+  __shared__ int soff[kTopkMaxSlices * kTopkWaves + 1];
+  __shared__ int fallback_s;
+  const int tok = blockIdx.x, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  // The segment counts (wave 0) and the first 64 entries of every segment (wave w: segments
+  // w, w + 8, ...) are loaded up front, together with the row length: their addresses do not
+  // depend on it. Entries past a count are read but never used (the workspace holds
+  // cap_seg >= 256 entries per segment); short rows do not use any of it.
+  const int n_seg = n_slices * kTopkWaves;                  // <= 128: two per lane of wave 0
+  const int64_t sbase = (int64_t)tok * n_seg;
+  int c0 = 0, c1 = 0;
+  if (w == 0) {
+    c0 = (2 * lane < n_seg) ? seg_cnt[sbase + 2 * lane] : 0;
+    c1 = (2 * lane + 1 < n_seg) ? seg_cnt[sbase + 2 * lane + 1] : 0;
   }
-  __syncthreads();
-  const int total = coff[n_chunks];
-  {
-    // all candidate loads in flight at once (at most 13 chunks x 4 per thread), then to LDS
-    constexpr int kPerChunk = kTopkMaxK / kTopkThreads;
-    uint32_t v[kTopkMaxChunks][kPerChunk];
+  constexpr int kSegPerWave = kTopkMaxSlices;
+  uint32_t kv[kSegPerWave];
+  int32_t pv[kSegPerWave];
 #pragma unroll
-    for (int c = 0; c < kTopkMaxChunks; ++c)
-#pragma unroll
-      for (int j = 0; j < kPerChunk; ++j) {
-        const int i = threadIdx.x + j * kTopkThreads;
-        const bool ok = c < n_chunks && i < coff[min(c + 1, n_chunks)] - coff[min(c, n_chunks)];
-        v[c][j] = ok ? cand_key[(tbase + c) * k + i] : 0u;
-      }
-#pragma unroll
-    for (int c = 0; c < kTopkMaxChunks; ++c)
-#pragma unroll
-      for (int j = 0; j < kPerChunk; ++j) {
-        const int i = threadIdx.x + j * kTopkThreads;
-        if (c < n_chunks && i < coff[c + 1] - coff[c]) keys[coff[c] + i] = v[c][j];
-      }
+  for (int u = 0; u < kSegPerWave; ++u) {
+    const int sg = w + kTopkWaves * u;
+    const int64_t at = (sbase + sg) * cap_seg + lane;
+    kv[u] = (sg < n_seg) ? cand_key[at] : 0u;
+    pv[u] = (sg < n_seg) ? cand_pos[at] : 0;
   }
-  __syncthreads();
-  int need = k;
-  const uint32_t thr = (total > k) ? radix_select<16>(keys, total, k, hist, state, need) : 0u;
+  const int n = visible(seq_lens, tok, q_len, n_max);
+  const float* row = scores + (int64_t)tok * n_max;
   int32_t* orow = out + (int64_t)tok * k;
-  int c = 0;                                               // chunk of the last candidate seen
-  ordered_emit(keys, total, thr, need, wsum,
-               [&](int i) {
-                 while (c + 1 < n_chunks && coff[c + 1] <= i) ++c;   // i increases within a thread
-                 return cand_pos[(tbase + c) * k + (i - coff[c])];
-               },
-               [&](int slot, int, int32_t pos) { orow[slot] = pos; });
-  for (int s = min(total, k) + threadIdx.x; s < k; s += kTopkThreads) orow[s] = -1;
+  auto lds_key = [&](int i) { return keys[i]; };
+  auto to_out = [&](int slot, int32_t p) { if (slot < k) orow[slot] = p; };   // slot < k always; kept as a bound
+  int need = k;
+  if (n <= kTopkTakeAll) {
+    // short row: all of it in LDS
+    if (n > 0) {
+      constexpr int kPer = kTopkTakeAll / kTopkThreads;
+      float v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kTopkThreads;
+        v[j] = (i < n) ? row[i] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kTopkThreads;
+        if (i < n) keys[i] = score_key(v[j]);
+      }
+      __syncthreads();
+      // thr 0 (n <= k): below every finite key, so every entry is emitted
+      const uint32_t thr = (n > k) ? select_kth_lds(lds_key, n, k, hist, wsum, state, red, need) : 0u;
+      ordered_emit(lds_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
+    }
+  } else {
+    if (w == 0) {
+      const int inc = wave_incl_sum(c0 + c1);
+      const int ex = inc - c0 - c1;
+      if (lane == 0) soff[0] = 0;
+      if (2 * lane < n_seg) soff[2 * lane + 1] = ex + c0;
+      if (2 * lane + 1 < n_seg) soff[2 * lane + 2] = ex + c0 + c1;
+      const bool over = __ballot(c0 > cap_seg || c1 > cap_seg) != 0ull;
+      const int o = __builtin_amdgcn_readlane(inc, 63);
+      if (lane == 0) fallback_s = over || o > kTopkCandCap || o < k;
+    }
+    __syncthreads();
+    const int total = soff[n_seg];
+    if (!fallback_s) {
+      // the lists into LDS in position order (segment by segment)
+      int longest = 0;
+#pragma unroll
+      for (int u = 0; u < kSegPerWave; ++u) {
+        const int sg = min(w + kTopkWaves * u, n_seg);
+        const int o = soff[sg], c = soff[min(sg + 1, n_seg)] - o;
+        longest = max(longest, c);
+        if (lane < c && o + lane < kTopkCandCap) { keys[o + lane] = kv[u]; pos[o + lane] = pv[u]; }
+      }
+      if (longest > 64) {                                    // entries 64.. of longer segments (rare)
+        for (int sg = w; sg < n_seg; sg += kTopkWaves) {
+          const int o = soff[sg], c = soff[sg + 1] - o;
+          for (int e = 64 + lane; e < c && o + e < kTopkCandCap; e += 64) {
+            const int64_t at = (sbase + sg) * cap_seg + e;
+            keys[o + e] = cand_key[at];
+            pos[o + e] = cand_pos[at];
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t thr = (total > k) ? select_kth_lds(lds_key, total, k, hist, wsum, state, red, need) : 0u;
+      ordered_emit(lds_key, total, thr, need, cnt, [&](int i) { return pos[i]; }, to_out);
+    } else {
+      // the whole row from memory (exact whatever the sample did)
+      auto mem_key = [&](int i) { return score_key(row[i]); };
+      const uint32_t thr = select_kth(mem_key, n, k, 0u, 31, 3, hist, wsum, state, need);
+      ordered_emit(mem_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
+    }
+  }
+  for (int s = min(n, k) + tid; s < k; s += kTopkThreads) orow[s] = -1;
 }
 
 hipError_t launch_topk(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t T,
                        int32_t q_len, int32_t k, void* workspace, int32_t* out, hipStream_t stream) {
-  const int32_t n_chunks = (int32_t)((n_max + kTopkChunk - 1) / kTopkChunk);
+  const TopkPlan pl = topk_plan(T, n_max);
+  const int64_t n_entries = (int64_t)T * pl.n_slices * 8 * pl.cap_seg;
   uint32_t* cand_key = (uint32_t*)workspace;
-  int32_t* cand_pos = (int32_t*)(cand_key + (int64_t)T * n_chunks * k);
-  int32_t* cand_cnt = cand_pos + (int64_t)T * n_chunks * k;
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)(T * n_chunks)), dim3(kTopkThreads), 0, stream,
-                     scores, n_max, seq_lens, q_len, k, n_chunks, cand_key, cand_pos, cand_cnt);
+  int32_t* cand_pos = (int32_t*)(cand_key + n_entries);
+  int32_t* seg_cnt = cand_pos + n_entries;
+  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)(T * pl.n_slices)), dim3(kTopkThreads), 0,
+                     stream, scores, n_max, seq_lens, q_len, k, pl.slice, pl.n_slices, pl.cap_seg,
+                     cand_key, cand_pos, seg_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(kTopkThreads), 0, stream, n_max,
-                     seq_lens, q_len, k, n_chunks, cand_key, cand_pos, cand_cnt, out);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(kTopkThreads), 0, stream, scores,
+                     n_max, seq_lens, q_len, k, pl.n_slices, pl.cap_seg, cand_key, cand_pos,
+                     seg_cnt, out);
   return hipGetLastError();
 }
 

@@ -192,8 +192,10 @@ def test_kv_layout_entry_points(lib):
 def test_topk_entry_point_rejects(lib):
     f = lib.mla_topk_indices
     ws = lib.mla_topk_workspace_size(4, 1000, 64)
-    assert ws == 4 * 1 * 64 * 8 + 4 * 1 * 4
-    assert lib.mla_topk_workspace_size(15, 149504, 2048) == 15 * 10 * 2048 * 8 + 15 * 10 * 4
+    # one slice of 2048 positions per token: 8 segments of 256 (key, position) entries + counts
+    assert ws == 4 * 8 * 256 * 8 + 4 * 8 * 4
+    # 15 slices of 10,240 positions per token, 8 segments each, 32768 // 120 = 273 entries each
+    assert lib.mla_topk_workspace_size(15, 149504, 2048) == 15 * 15 * 8 * (273 * 8 + 4)
     args = dict(s=FAKE, n=1000, sl=FAKE, B=2, q=2, k=64, o=FAKE, ws=FAKE, wb=1 << 20)
     def call(**kw):
         a = dict(args); a.update(kw)
@@ -201,7 +203,7 @@ def test_topk_entry_point_rejects(lib):
     assert call(s=None) == INVALID
     assert call(k=0) == UNSUPPORTED
     assert call(k=2049) == UNSUPPORTED
-    assert call(n=212993) == UNSUPPORTED
+    assert call(n=(1 << 20) + 1) == UNSUPPORTED
     assert call(B=0) == INVALID
     assert call(wb=100) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE
