@@ -387,14 +387,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
           float sv[8];
           float mx = -INFINITY;
+          if ((i + 1) * kTileRows <= n_rows) {               // full tile: no row mask
   #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const float4v sc = acc[rb][0] + acc[rb][1];
+            for (int rb = 0; rb < 2; ++rb) {
+              const float4v sc = acc[rb][0] + acc[rb][1];
   #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = i * kTileRows + 16 * rb + 4 * kg + e;
-              sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
-              mx = fmaxf(mx, sv[4 * rb + e]);
+              for (int e = 0; e < 4; ++e) {
+                sv[4 * rb + e] = sc[e] * a.scale_log2;
+                mx = fmaxf(mx, sv[4 * rb + e]);
+              }
+            }
+          } else {
+  #pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const float4v sc = acc[rb][0] + acc[rb][1];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int row = i * kTileRows + 16 * rb + 4 * kg + e;
+                sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sv[4 * rb + e]);
+              }
             }
           }
           mx = group4_max(mx);
