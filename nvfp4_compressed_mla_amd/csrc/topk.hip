@@ -33,10 +33,10 @@
 
 namespace mla {
 
-constexpr int kTopkThreads = 512;
-constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkPerThread = 16;                         // entries per thread per emit round
-constexpr int kTopkRound = kTopkThreads * kTopkPerThread;  // 8192: one round for LDS lists
+constexpr int kFilterThreads = 512;
+constexpr int kSegsPerSlice = kFilterThreads / 64;         // one list segment per filter wave
+constexpr int kMergeThreads = 1024;
+constexpr int kTopkRound = 8192;                           // emit round: one round for LDS lists
 constexpr int kTopkSampleRuns = kTopkSample / 8;           // runs of 8 consecutive positions
 constexpr int kFilterUnroll = 32;                          // loads in flight per lane
 constexpr int kBins = 4096;                                // 12-bit digits
@@ -70,16 +70,17 @@ __device__ __forceinline__ int wave_incl_sum(int x) {
   return (int)wave_scan((uint32_t)x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
-// Block-wide exclusive sum over the 512 threads (also the total). No barrier at the end: the
+// Block-wide exclusive sum over the NT threads (also the total). No barrier at the end: the
 // caller passes one before wsum is written again.
-__device__ __forceinline__ int block_excl_sum(int a, int& tot, int* wsum /* LDS 8 */) {
+template <int NT>
+__device__ __forceinline__ int block_excl_sum(int a, int& tot, int* wsum /* LDS NT / 64 */) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ia = wave_incl_sum(a);
   if (lane == 63) wsum[wv] = ia;
   __syncthreads();
   int pa = 0, ta = 0;
 #pragma unroll
-  for (int v = 0; v < kTopkWaves; ++v) {
+  for (int v = 0; v < NT / 64; ++v) {
     const int sa = wsum[v];
     pa += (v < wv) ? sa : 0;
     ta += sa;
@@ -89,23 +90,24 @@ __device__ __forceinline__ int block_excl_sum(int a, int& tot, int* wsum /* LDS 
 }
 
 // Smallest and largest of key_at(0 .. m-1) (m >= 1), the same in every thread.
-template <typename KeyAt>
-__device__ void block_minmax(KeyAt key_at, int m, uint32_t& mn, uint32_t& mx, uint32_t* red /* LDS 16 */) {
+template <int NT, typename KeyAt>
+__device__ void block_minmax(KeyAt key_at, int m, uint32_t& mn, uint32_t& mx, uint32_t* red /* LDS NT / 32 */) {
+  constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t a = 0xFFFFFFFFu, b = 0u;
-  for (int p = threadIdx.x; p < m; p += kTopkThreads) {
+  for (int p = threadIdx.x; p < m; p += NT) {
     const uint32_t v = key_at(p);
     a = min(a, v);
     b = max(b, v);
   }
   a = wave_scan(a, 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return min(x, y); });
   b = wave_scan(b, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
-  if (lane == 63) { red[wv] = a; red[kTopkWaves + wv] = b; }
+  if (lane == 63) { red[wv] = a; red[W + wv] = b; }
   __syncthreads();
   mn = red[0];
-  mx = red[kTopkWaves];
+  mx = red[W];
 #pragma unroll
-  for (int v = 1; v < kTopkWaves; ++v) { mn = min(mn, red[v]); mx = max(mx, red[kTopkWaves + v]); }
+  for (int v = 1; v < W; ++v) { mn = min(mn, red[v]); mx = max(mx, red[W + v]); }
 }
 
 // k-th largest of key_at(0 .. m-1) (1 <= k <= m), all keys >= base and key - base < 2^(hi+1).
@@ -114,42 +116,43 @@ __device__ void block_minmax(KeyAt key_at, int m, uint32_t& mn, uint32_t& mx, ui
 // zero: a lower bound of the k-th largest). Returns the threshold and, through `need`, how many
 // keys equal to it belong to the top k (all keys above it do). Each pass counts the offsets that
 // match the resolved prefix into a 4096-bin LDS histogram (two buffers: the next one is cleared
-// while this one fills); thread t owns bins 4095 - 8t .. 4088 - 8t, so a block scan of its 8-bin
-// sums gives the number of keys above them.
-template <typename KeyAt>
+// while this one fills); thread t owns the B = 4096 / NT bins 4095 - B t - j (j < B), so a block
+// scan of their sums gives the number of keys above them.
+template <int NT, typename KeyAt>
 __device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi, int max_passes,
                                uint32_t* hist /* LDS 2 x 4096 */, int* wsum, int* state, int& need) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, mask = (hi >= 31) ? 0u : ~((2u << hi) - 1u);
   int rem = k;
-  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  constexpr int B = kBins / NT;
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0;
   __syncthreads();
   for (int pass = 0; hi >= 0 && pass < max_passes; ++pass) {
     const int shift = max(hi - 11, 0);
     const uint32_t dmask = (2u << (hi - shift)) - 1u;
     uint32_t* h = hist + (pass & 1) * kBins;
     uint32_t* h_next = hist + ((pass + 1) & 1) * kBins;
-    for (int p0 = tid; p0 < m; p0 += 8 * kTopkThreads) {   // 8 reads in flight per lane
+    for (int p0 = tid; p0 < m; p0 += 8 * NT) {             // 8 reads in flight per lane
       uint32_t dd[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int p = p0 + j * kTopkThreads;
+        const int p = p0 + j * NT;
         dd[j] = (p < m) ? key_at(p) - base : 0u;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (p0 + j * kTopkThreads < m && (dd[j] & mask) == prefix) atomicAdd(&h[(dd[j] >> shift) & dmask], 1u);
+        if (p0 + j * NT < m && (dd[j] & mask) == prefix) atomicAdd(&h[(dd[j] >> shift) & dmask], 1u);
     }
-    for (int i = tid; i < kBins; i += kTopkThreads) h_next[i] = 0;
+    for (int i = tid; i < kBins; i += NT) h_next[i] = 0;
     __syncthreads();
-    int c[8], sum = 0;
+    int c[B], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { c[j] = (int)h[kBins - 1 - 8 * tid - j]; sum += c[j]; }
+    for (int j = 0; j < B; ++j) { c[j] = (int)h[kBins - 1 - B * tid - j]; sum += c[j]; }
     int tot;
-    int run = block_excl_sum(sum, tot, wsum);
+    int run = block_excl_sum<NT>(sum, tot, wsum);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (run < rem && run + c[j] >= rem) { state[0] = kBins - 1 - 8 * tid - j; state[1] = rem - run; }
+    for (int j = 0; j < B; ++j) {
+      if (run < rem && run + c[j] >= rem) { state[0] = kBins - 1 - B * tid - j; state[1] = rem - run; }
       run += c[j];
     }
     __syncthreads();
@@ -163,44 +166,45 @@ __device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi
 }
 
 // k-th largest of keys that sit in LDS (1 <= k <= m), on offsets from the smallest key.
-template <typename KeyAt>
+template <int NT, typename KeyAt>
 __device__ uint32_t select_kth_lds(KeyAt key_at, int m, int k, uint32_t* hist, int* wsum, int* state,
                                    uint32_t* red, int& need) {
   uint32_t mn, mx;
-  block_minmax(key_at, m, mn, mx, red);
+  block_minmax<NT>(key_at, m, mn, mx, red);
   if (mn == mx) { need = k; return mx; }
-  return select_kth(key_at, m, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
+  return select_kth<NT>(key_at, m, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
 }
 
 // Emit, in list order, the entries of key_at(0 .. m-1) above thr plus the first `need` equal to
-// it, as emit(slot, payload(i)). Rounds of 8192 entries: entry r0 + 512 j + tid is thread tid's
+// it, as emit(slot, payload(i)). Rounds of 8192 entries: entry r0 + NT j + tid is thread tid's
 // j-th, so an entry's rank is (counts of the waves' ballots of earlier (j, wave) pairs, scanned by
 // wave 0) + (its rank in its own ballot).
-template <typename KeyAt, typename Payload, typename Emit>
-__device__ void ordered_emit(KeyAt key_at, int m, uint32_t thr, int need, int* cnt /* LDS 514 */,
+template <int NT, typename KeyAt, typename Payload, typename Emit>
+__device__ void ordered_emit(KeyAt key_at, int m, uint32_t thr, int need, int* cnt /* LDS 258 */,
                              Payload payload, Emit emit) {
-  constexpr int kQ = kTopkPerThread * kTopkWaves;          // 128 (j, wave) pairs
+  constexpr int kPer = kTopkRound / NT, kW = NT / 64;
+  constexpr int kQ = kPer * kW;          // 128 (j, wave) pairs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int gc = 0, ec = 0;                                     // carried over rounds
   for (int r0 = 0; r0 < m; r0 += kTopkRound) {
-    const int jn = min(kTopkPerThread, (m - r0 + kTopkThreads - 1) / kTopkThreads);   // rows present
-    uint32_t kk[kTopkPerThread];
-    int32_t pl[kTopkPerThread];
+    const int jn = min(kPer, (m - r0 + NT - 1) / NT);   // rows present
+    uint32_t kk[kPer];
+    int32_t pl[kPer];
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) {
-      const int p = r0 + j * kTopkThreads + tid;
+    for (int j = 0; j < kPer; ++j) {
+      const int p = r0 + j * NT + tid;
       kk[j] = (p < m) ? key_at(p) : 0u;
       pl[j] = (p < m) ? payload(p) : 0;
     }
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       if (j >= jn) {                                       // workgroup-uniform
-        if (lane == 0) { cnt[j * kTopkWaves + w] = 0; cnt[kQ + j * kTopkWaves + w] = 0; }
+        if (lane == 0) { cnt[j * kW + w] = 0; cnt[kQ + j * kW + w] = 0; }
         continue;
       }
-      const bool in = r0 + j * kTopkThreads + tid < m;
+      const bool in = r0 + j * NT + tid < m;
       const uint64_t bg = __ballot(in && kk[j] > thr), be = __ballot(in && kk[j] == thr);
-      if (lane == 0) { cnt[j * kTopkWaves + w] = __popcll(bg); cnt[kQ + j * kTopkWaves + w] = __popcll(be); }
+      if (lane == 0) { cnt[j * kW + w] = __popcll(bg); cnt[kQ + j * kW + w] = __popcll(be); }
     }
     __syncthreads();
     if (w == 0) {
@@ -216,14 +220,14 @@ __device__ void ordered_emit(KeyAt key_at, int m, uint32_t thr, int need, int* c
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       if (j >= jn) break;                                  // workgroup-uniform
-      const bool in = r0 + j * kTopkThreads + tid < m;
+      const bool in = r0 + j * NT + tid < m;
       const bool gt = in && kk[j] > thr, eq = in && kk[j] == thr;
       const uint64_t bg = __ballot(gt), be = __ballot(eq);
-      const int gb = gc + cnt[j * kTopkWaves + w] +
+      const int gb = gc + cnt[j * kW + w] +
                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
-      const int eb = ec + cnt[kQ + j * kTopkWaves + w] +
+      const int eb = ec + cnt[kQ + j * kW + w] +
                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
       if (gt) emit(gb + min(eb, need), pl[j]);
       else if (eq && eb < need) emit(gb + eb, pl[j]);
@@ -255,22 +259,22 @@ __device__ __forceinline__ int sample_pos(int i, int n) {
   return (int)(((int64_t)(i >> 3) * n) / kTopkSampleRuns) + (i & 7);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(
+__global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t n_max, const int32_t* __restrict__ seq_lens,
     int32_t q_len, int32_t k, int64_t slice, int32_t n_slices, int32_t cap_seg,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_pos, int32_t* __restrict__ seg_cnt) {
   __shared__ uint32_t skeys[kTopkSample];
   __shared__ uint32_t hist[2 * kBins];
-  __shared__ int wsum[kTopkWaves];
+  __shared__ int wsum[kFilterThreads / 64];
   __shared__ int state[2];
   const int tok = blockIdx.x / n_slices, g = blockIdx.x - tok * n_slices;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t seg = ((int64_t)tok * n_slices + g) * kTopkWaves + w;
+  const int64_t seg = ((int64_t)tok * n_slices + g) * kSegsPerSlice + w;
   const float* row = scores + (int64_t)tok * n_max;
   // this wave's segment of the slice, in batches of kFilterUnroll rows of 64 positions; the
   // first batch is loaded before the row length is known (bounded by the row's n_max entries)
   // and stays in flight while the cut is found
-  const int64_t seg_len = slice / kTopkWaves;
+  const int64_t seg_len = slice / kSegsPerSlice;
   const int64_t p_begin = (int64_t)g * slice + w * seg_len;
   auto load_batch = [&](int64_t b0, int64_t lim, float (&v)[kFilterUnroll]) {
 #pragma unroll
@@ -290,13 +294,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(
   // the sample (identical in every workgroup of the token) and its cut: the top 24 bits of its
   // r-th largest key
 #pragma unroll
-  for (int j = 0; j < kTopkSample / kTopkThreads; ++j) {
-    const int i = threadIdx.x * (kTopkSample / kTopkThreads) + j;
+  for (int j = 0; j < kTopkSample / kFilterThreads; ++j) {
+    const int i = threadIdx.x * (kTopkSample / kFilterThreads) + j;
     skeys[i] = score_key(row[sample_pos(i, n)]);
   }
   __syncthreads();
   int unused;
-  const uint32_t cut = select_kth([&](int i) { return skeys[i]; }, kTopkSample, sample_rank(k, n),
+  const uint32_t cut = select_kth<kFilterThreads>([&](int i) { return skeys[i]; }, kTopkSample, sample_rank(k, n),
                                   0u, 31, 2, hist, wsum, state, unused);
   uint32_t* ck = cand_key + seg * cap_seg;
   int32_t* cp = cand_pos + seg * cap_seg;
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(
   if (lane == 0) seg_cnt[seg] = cnt;                       // the true count, even past cap_seg
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     const float* __restrict__ scores, int64_t n_max, const int32_t* __restrict__ seq_lens,
     int32_t q_len, int32_t k, int32_t n_slices, int32_t cap_seg,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
@@ -332,10 +336,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   __shared__ int32_t pos[kTopkCandCap];
   __shared__ uint32_t hist[2 * kBins];
   __shared__ int state[2];
-  __shared__ int wsum[kTopkWaves];
-  __shared__ uint32_t red[2 * kTopkWaves];
-  __shared__ int cnt[2 * kTopkPerThread * kTopkWaves + 2];
-  __shared__ int soff[kTopkMaxSlices * kTopkWaves + 1];
+  constexpr int NT = kMergeThreads, W = NT / 64;
+  __shared__ int wsum[W];
+  __shared__ uint32_t red[2 * W];
+  __shared__ int cnt[2 * 128 + 2];
+  __shared__ int soff[kTopkMaxSlices * kSegsPerSlice + 1];
   __shared__ int fallback_s;
   const int tok = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -343,19 +348,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   // w, w + 8, ...) are loaded up front, together with the row length: their addresses do not
   // depend on it. Entries past a count are read but never used (the workspace holds
   // cap_seg >= 256 entries per segment); short rows do not use any of it.
-  const int n_seg = n_slices * kTopkWaves;                  // <= 128: two per lane of wave 0
+  const int n_seg = n_slices * kSegsPerSlice;               // <= 128: two per lane of wave 0
   const int64_t sbase = (int64_t)tok * n_seg;
   int c0 = 0, c1 = 0;
   if (w == 0) {
     c0 = (2 * lane < n_seg) ? seg_cnt[sbase + 2 * lane] : 0;
     c1 = (2 * lane + 1 < n_seg) ? seg_cnt[sbase + 2 * lane + 1] : 0;
   }
-  constexpr int kSegPerWave = kTopkMaxSlices;
+  constexpr int kSegPerWave = kTopkMaxSlices * kSegsPerSlice / W;
   uint32_t kv[kSegPerWave];
   int32_t pv[kSegPerWave];
 #pragma unroll
   for (int u = 0; u < kSegPerWave; ++u) {
-    const int sg = w + kTopkWaves * u;
+    const int sg = w + W * u;
     const int64_t at = (sbase + sg) * cap_seg + lane;
     kv[u] = (sg < n_seg) ? cand_key[at] : 0u;
     pv[u] = (sg < n_seg) ? cand_pos[at] : 0;
@@ -369,22 +374,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   if (n <= kTopkTakeAll) {
     // short row: all of it in LDS
     if (n > 0) {
-      constexpr int kPer = kTopkTakeAll / kTopkThreads;
+      constexpr int kPer = kTopkTakeAll / NT;
       float v[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * kTopkThreads;
+        const int i = tid + j * NT;
         v[j] = (i < n) ? row[i] : 0.0f;
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * kTopkThreads;
+        const int i = tid + j * NT;
         if (i < n) keys[i] = score_key(v[j]);
       }
       __syncthreads();
       // thr 0 (n <= k): below every finite key, so every entry is emitted
-      const uint32_t thr = (n > k) ? select_kth_lds(lds_key, n, k, hist, wsum, state, red, need) : 0u;
-      ordered_emit(lds_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
+      const uint32_t thr = (n > k) ? select_kth_lds<NT>(lds_key, n, k, hist, wsum, state, red, need) : 0u;
+      ordered_emit<NT>(lds_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
     }
   } else {
     if (w == 0) {
@@ -404,13 +409,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
       int longest = 0;
 #pragma unroll
       for (int u = 0; u < kSegPerWave; ++u) {
-        const int sg = min(w + kTopkWaves * u, n_seg);
+        const int sg = min(w + W * u, n_seg);
         const int o = soff[sg], c = soff[min(sg + 1, n_seg)] - o;
         longest = max(longest, c);
         if (lane < c && o + lane < kTopkCandCap) { keys[o + lane] = kv[u]; pos[o + lane] = pv[u]; }
       }
       if (longest > 64) {                                    // entries 64.. of longer segments (rare)
-        for (int sg = w; sg < n_seg; sg += kTopkWaves) {
+        for (int sg = w; sg < n_seg; sg += W) {
           const int o = soff[sg], c = soff[sg + 1] - o;
           for (int e = 64 + lane; e < c && o + e < kTopkCandCap; e += 64) {
             const int64_t at = (sbase + sg) * cap_seg + e;
@@ -420,31 +425,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
         }
       }
       __syncthreads();
-      const uint32_t thr = (total > k) ? select_kth_lds(lds_key, total, k, hist, wsum, state, red, need) : 0u;
-      ordered_emit(lds_key, total, thr, need, cnt, [&](int i) { return pos[i]; }, to_out);
+      const uint32_t thr = (total > k) ? select_kth_lds<NT>(lds_key, total, k, hist, wsum, state, red, need) : 0u;
+      ordered_emit<NT>(lds_key, total, thr, need, cnt, [&](int i) { return pos[i]; }, to_out);
     } else {
       // the whole row from memory (exact whatever the sample did)
       auto mem_key = [&](int i) { return score_key(row[i]); };
-      const uint32_t thr = select_kth(mem_key, n, k, 0u, 31, 3, hist, wsum, state, need);
-      ordered_emit(mem_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
+      const uint32_t thr = select_kth<NT>(mem_key, n, k, 0u, 31, 3, hist, wsum, state, need);
+      ordered_emit<NT>(mem_key, n, thr, need, cnt, [](int i) { return i; }, to_out);
     }
   }
-  for (int s = min(n, k) + tid; s < k; s += kTopkThreads) orow[s] = -1;
+  for (int s = min(n, k) + tid; s < k; s += NT) orow[s] = -1;
 }
 
 hipError_t launch_topk(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t T,
                        int32_t q_len, int32_t k, void* workspace, int32_t* out, hipStream_t stream) {
   const TopkPlan pl = topk_plan(T, n_max);
-  const int64_t n_entries = (int64_t)T * pl.n_slices * 8 * pl.cap_seg;
+  const int64_t n_entries = (int64_t)T * pl.n_slices * kSegsPerSlice * pl.cap_seg;
   uint32_t* cand_key = (uint32_t*)workspace;
   int32_t* cand_pos = (int32_t*)(cand_key + n_entries);
   int32_t* seg_cnt = cand_pos + n_entries;
-  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)(T * pl.n_slices)), dim3(kTopkThreads), 0,
+  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)(T * pl.n_slices)), dim3(kFilterThreads), 0,
                      stream, scores, n_max, seq_lens, q_len, k, pl.slice, pl.n_slices, pl.cap_seg,
                      cand_key, cand_pos, seg_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(kTopkThreads), 0, stream, scores,
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(kMergeThreads), 0, stream, scores,
                      n_max, seq_lens, q_len, k, pl.n_slices, pl.cap_seg, cand_key, cand_pos,
                      seg_cnt, out);
   return hipGetLastError();
