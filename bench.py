@@ -65,7 +65,7 @@ class SparseWorkload:
     """
 
     def __init__(self, name, B, q_len, H, ctx, topk, append_rows, rotations, seed, device,
-                 q_lens=None, keep_latent=False, fmt="nvfp4"):
+                 q_lens=None, keep_latent=False, fmt="nvfp4", overlap=None):
         import torch
         from nvfp4_compressed_mla_amd import workloads as wl
         import nvfp4_compressed_mla_amd as m
@@ -97,7 +97,10 @@ class SparseWorkload:
                                     for b in range(B)])
         self.rot = rotations
         self.q = [wl.gen_queries(B, q_len, H, "bf16", seed + 100 + r, device) for r in range(rotations)]
-        if q_lens is None and len(set(self.ctx)) == 1 and self.ctx[0] >= topk:
+        if overlap is not None:
+            self.idx = [wl.gen_topk_overlap(B, q_len, topk, self.ctx, overlap, seed + 200 + r, device)
+                        for r in range(rotations)]
+        elif q_lens is None and len(set(self.ctx)) == 1 and self.ctx[0] >= topk:
             self.idx = [wl.gen_topk_batched(B, q_len, topk, self.ctx[0], seed + 200 + r, device)
                         for r in range(rotations)]
         else:
@@ -425,7 +428,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way, kv_transfer, topk (default all; 'none' = --no-extra)")
+                         "mixed, three_way, mtp_overlap, kv_transfer, topk (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -517,7 +520,7 @@ def main():
     }
 
     wanted = set() if args.no_extra or args.extras == "none" else (
-        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "kv_transfer", "topk"} if args.extras == "all"
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
         extra = {}
@@ -576,6 +579,23 @@ def main():
                     del w2
                     torch.cuda.empty_cache()
                 extra[f"three_way_{shape}"] = cmp
+        if "mtp_overlap" in wanted:
+            # the MTP shape under an overlap model: the 15 query tokens of a request keep a share of
+            # one base set of positions (ascending lists); the splits of a request's tokens run on
+            # one XCD, so a row shared by several tokens is fetched from HBM once and then read
+            # from that XCD's L2
+            ov = {}
+            for f in (0.0, 0.5, 0.9):
+                log(f"[bench] extra: mtp_overlap {f}")
+                w2 = SparseWorkload("mtp_ov", 16, 15, 64, [149504] * 16, 2048, 0, 6, 1005, dev, overlap=f)
+                res = run_config(w2, 192, 24, 32)
+                uniq = [len(set(w2.idx[0][b].flatten().tolist())) for b in range(16)]
+                res["distinct_rows_per_request"] = round(sum(uniq) / len(uniq), 1)
+                res["gathered_rows_per_request"] = 15 * 2048
+                ov[f"overlap_{f}"] = res
+                del w2
+                torch.cuda.empty_cache()
+            extra["mtp_overlap_B16_q15_H64"] = ov
         if "topk" in wanted:
             extra["topk_2048"] = topk_bench(dev)
         if "kv_transfer" in wanted:

@@ -146,6 +146,30 @@ def gen_topk(B: int, q_len: int, k: int, ctx: list, seed: int, device="cpu", q_l
     return out
 
 
+def gen_topk_overlap(B: int, q_len: int, k: int, ctx: list, overlap: float, seed: int, device="cpu"):
+    """Top-k lists int32 [B, q_len, k] whose tokens share rows within a request (an overlap
+    model of multi-token decode: the query tokens of one request pick mostly the same positions).
+
+    Per request: a base set of k distinct uniform positions in [0, ctx_b). Each token keeps a
+    uniform subset of round(overlap * k) base positions and adds k - that many distinct positions
+    from outside the base set. Lists are in ascending position order. Requires ctx_b >= 2k.
+    """
+    g = _gen(seed, device)
+    keep = int(round(overlap * k))
+    out = torch.empty((B, q_len, k), dtype=torch.int32, device=device)
+    for b in range(B):
+        c = int(ctx[b])
+        if c < 2 * k:
+            raise ValueError("gen_topk_overlap needs ctx >= 2k")
+        perm = torch.randperm(c, generator=g, device=device)
+        base, rest = perm[:k], perm[k:]
+        for t in range(q_len):
+            sub = base[torch.randperm(k, generator=g, device=device)[:keep]]
+            fresh = rest[torch.randperm(c - k, generator=g, device=device)[:k - keep]]
+            out[b, t] = torch.sort(torch.cat([sub, fresh])).values.to(torch.int32)
+    return out
+
+
 def gen_topk_batched(B: int, q_len: int, k: int, ctx: int, seed: int, device="cpu"):
     """Same distribution as ``gen_topk`` for a common context >= k, drawn for all tokens at once."""
     g = _gen(seed, device)

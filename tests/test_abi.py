@@ -207,3 +207,22 @@ def test_topk_entry_point_rejects(lib):
     assert call(B=0) == INVALID
     assert call(wb=100) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE
+
+
+def test_overlap_list_generator():
+    """The overlap-model input generator: distinct ascending positions, the stated share of one
+    base set per request (host-side, no GPU)."""
+    import numpy as np
+    from nvfp4_compressed_mla_amd import workloads as wl
+    idx = wl.gen_topk_overlap(3, 5, 64, [500, 200, 129], 0.75, 11, "cpu").numpy()
+    for b in range(3):
+        rows = [set(idx[b, t].tolist()) for t in range(5)]
+        for t in range(5):
+            assert len(rows[t]) == 64 and (np.diff(idx[b, t]) > 0).all()
+            assert idx[b, t].min() >= 0 and idx[b, t].max() < [500, 200, 129][b]
+        union = set().union(*rows)
+        assert len(union) <= 64 + 5 * 16          # base set + 16 fresh positions per token
+        inter = set.intersection(*rows)
+        assert len(inter) <= 48
+    with pytest.raises(ValueError):
+        wl.gen_topk_overlap(1, 1, 64, [100], 0.5, 1, "cpu")

@@ -154,3 +154,15 @@ def test_uniform_scores_give_mean():
         out, lse = _sparse(case, splits)
         assert torch.allclose(out[0, 0].double(), mean.expand(16, 512), rtol=0, atol=atol), splits
         assert torch.allclose(lse[0, 0], torch.full_like(lse[0, 0], math.log(96)), atol=1e-5), splits
+
+
+def test_overlapping_lists_across_query_tokens():
+    """Multi-token decode lists under an overlap model: the query tokens of a request share 80% of
+    their positions (ascending lists), so rows repeat across the workgroups of one request."""
+    print("case: overlap 0.8, B=2, q_len=4, H=64, ctx [5000, 4200], k=1024", flush=True)
+    fn = lambda B, q, k, ctx, seed, dev: wl.gen_topk_overlap(B, q, k, ctx, 0.8, seed, dev)
+    case = th.build_case(2, 4, 64, [5000, 4200], 1024, seed=321, topk_fn=fn)
+    ref_o, ref_l = th.oracle_sparse(case)
+    for s in (0, 1, 3):
+        out, lse = _sparse(case, s)
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"overlap 0.8 splits={s}")
