@@ -540,6 +540,14 @@ def main():
             log("[bench] extra: dense_B8_H64_146K")
             dw = DenseWorkload(8, 64, 149504, 4096, 3, 1003, dev)
             extra["dense_B8_H64_146K_split4096"] = run_config(dw, 48, 6, 24)
+            # the split size that fits the launch in one wave of workgroups (37 splits of 4096
+            # positions give 296 workgroups for 256 compute units)
+            st = m.mla_dense_decode_split_tokens(8, 64, dw.tables[0].shape[1])
+            del dw
+            torch.cuda.empty_cache()
+            log(f"[bench] extra: dense_B8_H64_146K one-wave split ({st} positions)")
+            dw = DenseWorkload(8, 64, 149504, st, 3, 1003, dev)
+            extra["dense_B8_H64_146K_one_wave"] = {"split_tokens": st, **run_config(dw, 48, 6, 24)}
             del dw
             torch.cuda.empty_cache()
         if "mixed" in wanted:

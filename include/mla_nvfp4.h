@@ -96,6 +96,13 @@ int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk
 /* Number of row splits mla_dense_decode uses: ceil(max_pages*64 / split_tokens). */
 int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens);
 
+/* A split size for mla_dense_decode that puts the whole launch in one wave of workgroups: the
+ * largest split count s with num_tokens * ceil(H/64) * s <= 256 (one workgroup per compute
+ * unit), then split_tokens = ceil(max_pages*64 / s) rounded up to a multiple of 64 and clamped
+ * to [64, 8192]. Returns 4096 for invalid arguments. (A fixed 4096-token split can leave a short
+ * second wave: 8 tokens x 37 splits = 296 workgroups at 149,504 positions.) */
+int32_t mla_dense_decode_split_tokens(int32_t num_tokens, int32_t H, int32_t max_pages);
+
 /* Sparse decode (page section "Native NVFP4 sparse MLA decode kernel").
  *   q          [B, q_len, H, 576] contiguous, bf16 or fp32 (q_dtype): absorbed queries, latent
  *              part first (512), rope part last (64).

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     mla_decode_workspace_size,
     mla_dense_decode,
     mla_dense_decode_num_splits,
+    mla_dense_decode_split_tokens,
     mla_fp8_append,
     mla_fp8_dense_decode,
     mla_fp8_sparse_decode,

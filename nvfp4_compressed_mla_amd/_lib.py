@@ -27,6 +27,7 @@ EXPORTED = [
     "mla_decode_workspace_size",
     "mla_sparse_decode_num_splits",
     "mla_dense_decode_num_splits",
+    "mla_dense_decode_split_tokens",
     "mla_sparse_decode",
     "mla_dense_decode",
     "mla_nvfp4_dequantize_rows",
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_sparse_decode_num_splits.restype = i32
     lib.mla_dense_decode_num_splits.argtypes = [i32, i32]
     lib.mla_dense_decode_num_splits.restype = i32
+    lib.mla_dense_decode_split_tokens.argtypes = [i32, i32, i32]
+    lib.mla_dense_decode_split_tokens.restype = i32
     lib.mla_sparse_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
                                       i32, f32, i32, vp, vp, vp, sz, vp]
     lib.mla_sparse_decode.restype = ctypes.c_int
@@ -197,6 +200,10 @@ def mla_sparse_decode_num_splits(num_tokens: int, H: int, topk: int, max_splits:
 
 def mla_dense_decode_num_splits(max_pages: int, split_tokens: int) -> int:
     return int(load_library().mla_dense_decode_num_splits(max_pages, split_tokens))
+
+
+def mla_dense_decode_split_tokens(num_tokens: int, H: int, max_pages: int) -> int:
+    return int(load_library().mla_dense_decode_split_tokens(num_tokens, H, max_pages))
 
 
 def _q_dtype(q):

@@ -50,7 +50,7 @@ mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_
   return MLA_OK;
 }
 
-// Decode workgroups resident at once: one per compute unit (512 threads, ~120 KB of LDS).
+// Decode workgroups resident at once: one per compute unit (768 threads, up to 160 KB of LDS).
 int waves_capacity(int32_t) { return kComputeUnits; }
 
 size_t ws_bytes(int64_t T, int64_t H, int64_t S) {
@@ -193,6 +193,18 @@ int32_t mla_sparse_decode_num_splits(int32_t num_tokens, int32_t H, int32_t topk
   if (s > 16) s = 16;
   if (s > cap_by_rows) s = cap_by_rows;
   return (int32_t)s;
+}
+
+int32_t mla_dense_decode_split_tokens(int32_t num_tokens, int32_t H, int32_t max_pages) {
+  if (num_tokens < 1 || H < 16 || max_pages < 1) return 4096;
+  const int64_t items = (int64_t)num_tokens * head_groups(H);
+  int64_t s = waves_capacity(H) / items;                 // splits per token that fit one wave
+  if (s < 1) s = 1;
+  const int64_t rows = (int64_t)max_pages * MLA_PAGE_ROWS;
+  int64_t st = (rows + s - 1) / s;
+  st = (st + MLA_PAGE_ROWS - 1) / MLA_PAGE_ROWS * MLA_PAGE_ROWS;
+  const int64_t lo = MLA_PAGE_ROWS, hi = (int64_t)mla::kMaxDensePages * MLA_PAGE_ROWS;
+  return (int32_t)(st < lo ? lo : (st > hi ? hi : st));
 }
 
 int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens) {

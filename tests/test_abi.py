@@ -226,3 +226,16 @@ def test_overlap_list_generator():
         assert len(inter) <= 48
     with pytest.raises(ValueError):
         wl.gen_topk_overlap(1, 1, 64, [100], 0.5, 1, "cpu")
+
+
+def test_dense_one_wave_split_helper(lib):
+    """The dense split-size helper: one wave of 256 workgroups where the 8192-row cap allows."""
+    f, ns = lib.mla_dense_decode_split_tokens, lib.mla_dense_decode_num_splits
+    assert f(8, 64, 2339) == 4736 and ns(2339, 4736) == 32           # 8 x 32 = 256 workgroups
+    for T, H, P in [(1, 16, 100), (3, 64, 2336), (8, 64, 2336), (16, 80, 3200), (64, 64, 500)]:
+        st = f(T, H, P)
+        assert st % 64 == 0 and 64 <= st <= 8192
+        groups = -(-(H // 16) // 4)
+        if st < 8192 and st > 64:
+            assert T * groups * ns(P, st) <= 256
+    assert f(0, 64, 10) == 4096 and f(4, 8, 10) == 4096

@@ -130,10 +130,11 @@ def test_topk_all_equals_dense():
 
 
 def test_dense_causal_and_splits():
-    print("case: dense q_len=3 causal, split 64/512/4096", flush=True)
+    print("case: dense q_len=3 causal, split 64/512/4096/one-wave", flush=True)
     case = th.build_case(2, 3, 32, [2000, 700], 0, seed=12)
     ref_o, ref_l = th.oracle_dense(case)
-    for st in (64, 512, 4096):
+    auto = _m().mla_dense_decode_split_tokens(6, 32, case.block_table.shape[1])
+    for st in (64, 512, 4096, auto):
         out, lse = _dense(case, st)
         th.assert_parity(out, lse, ref_o, ref_l, what=f"dense split_tokens={st}")
 
