@@ -4,11 +4,9 @@
 // section "Making room for low-latency decode": the MLA latent is compressed to NVFP4 -- 4-bit
 // values with one FP8 scale per 16 values -- and the 64-value rope part stays FP8) is a pure
 // streaming pass: 1152 bytes of bf16 in, one 352-byte row out, so it is bound by HBM bandwidth.
-// One wavefront owns one row: lane l reads latent elements 8l..8l+7 with one 16-byte load (its
-// group of 16 is shared with lane l^1), and rope element l. Group maxima are combined across the
-// lane pair, the scale byte and the eight 4-bit codes are computed with exact integer/compare
-// arithmetic, and the row leaves as dword stores: 64 code dwords, 8 scale dwords (gathered with
-// lane shuffles) and 16 rope dwords.
+// Each lane encodes one 16-value group with exact integer/compare arithmetic (scale byte, then
+// sixteen 4-bit codes) and two rope values; a row leaves as two stores: 256 code bytes (8 per
+// lane), then 8 scale dwords and 16 rope dwords gathered with lane shuffles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,52 +17,97 @@ namespace mla {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Layout: lane l of a wavefront owns group g = l & 31 (16 latent values) of row 2i + (l >> 5),
+// so the per-group work (amax, scale byte, grid midpoints) is done once per group and each half
+// of the wave encodes one row. A wave takes kAppendPairs row pairs per iteration and issues all
+// their loads (slots, latent, rope) before encoding the first, which keeps several rows in flight.
+// The kernel is bound by its integer/compare arithmetic more than by its 1,512 bytes per row.
+constexpr int kAppendPairs = 2;
+constexpr int kAppendRowsPerIter = 2 * kAppendPairs;
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(256) void quantize_append_kernel(
     const uint16_t* __restrict__ latent, int64_t latent_stride,
     const uint16_t* __restrict__ rope, int64_t rope_stride,
     const int64_t* __restrict__ slots, int64_t n_rows,
     uint8_t* __restrict__ cache, int64_t page_stride, int64_t cache_bytes) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int half = lane >> 5, g = lane & 31;
+  const int64_t n_iters = (n_rows + kAppendRowsPerIter - 1) / kAppendRowsPerIter;
   const int64_t wave_stride = (int64_t)gridDim.x * 4;
-  for (int64_t row = wave0; row < n_rows; row += wave_stride) {
-    const int64_t slot = slots[row];
-    if (slot < 0) continue;                                   // wave-uniform
-    const int64_t off = (slot / kPageRows) * page_stride + (slot % kPageRows) * kRowBytes;
-    if (off < 0 || off + kRowBytes > cache_bytes) continue;   // outside the cache: not written
-
-    const uint4v x8 = *(const uint4v*)(latent + row * latent_stride + lane * 8);
-    const uint32_t rbits = rope[row * rope_stride + lane];
-
-    float v[8];
+  // Workgroup b runs on XCD b % 8 (the grid is a multiple of 8). Consecutive rows are given to
+  // workgroups of one XCD, so the rows of a page, whose 352-byte rows share 128-byte lines, are
+  // written through one L2.
+  const int64_t wg = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  for (int64_t it = wg * 4 + (threadIdx.x >> 6); it < n_iters; it += wave_stride) {
+    const int64_t row0 = it * kAppendRowsPerIter;
+    // Branch-free loads: rows past the end re-read the last row and are not written.
+    const int64_t slot_l = slots[min(row0 + min(lane, kAppendRowsPerIter - 1), n_rows - 1)];
+    uint4v xa[kAppendPairs], xb[kAppendPairs];
+    uint32_t ra[kAppendPairs], rb[kAppendPairs];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_bits_to_float(x8[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_bits_to_float(x8[i] >> 16);
+    for (int p = 0; p < kAppendPairs; ++p) {
+      const int64_t row = min(row0 + 2 * p + half, n_rows - 1);
+      const uint16_t* lrow = latent + row * latent_stride + 16 * g;
+      xa[p] = *(const uint4v*)lrow;
+      xb[p] = *(const uint4v*)(lrow + 8);
+      ra[p] = rope[row * rope_stride + g];               // rope element g
+      rb[p] = rope[row * rope_stride + 32 + g];          // rope element 32 + g
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));                  // the other half of the group
+    for (int p = 0; p < kAppendPairs; ++p) {
+      const int64_t row = row0 + 2 * p + half;
+      const int64_t slot = half ? readlane64(slot_l, 2 * p + 1) : readlane64(slot_l, 2 * p);
+      const int64_t off = (slot / kPageRows) * page_stride + (slot % kPageRows) * kRowBytes;
+      // rows past the end, slots of -1 and slots outside the cache are not written
+      const bool write = row < n_rows && slot >= 0 && off >= 0 && off + kRowBytes <= cache_bytes;
 
-    const uint32_t sbyte = e4m3_encode(amax / 6.0f);          // IEEE division, then RNE to E4M3
-    const float s = e4m3_to_float(sbyte);
-    uint32_t codes = 0;
+      float v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) codes |= e2m1_encode(v[i], s) << (4 * i);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_float(xa[p][i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_float(xa[p][i] >> 16);
+        v[8 + 2 * i] = bf16_bits_to_float(xb[p][i] & 0xFFFFu);
+        v[8 + 2 * i + 1] = bf16_bits_to_float(xb[p][i] >> 16);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+      // amax * fl(1/6) rounds to the same E4M3 byte as the exact quotient amax / 6 for every
+      // finite bf16 amax (checked exhaustively on the host), at the cost of one multiply.
+      const uint32_t sbyte = e4m3_encode2_hw(amax * (1.0f / 6.0f), 0.0f) & 0xFFu;
+      const E2m1Midpoints mid = e2m1_midpoints(e4m3_to_float_hw(sbyte));
+      uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c0 |= e2m1_encode(v[i], mid) << (4 * i);
+        c1 |= e2m1_encode(v[8 + i], mid) << (4 * i);
+      }
+      const uint32_t rpair = e4m3_encode2_hw(bf16_bits_to_float(ra[p]), bf16_bits_to_float(rb[p]));
+      const uint32_t rba = rpair & 0xFFu, rbb = rpair >> 8;
 
-    const uint32_t rbyte = e4m3_encode(bf16_bits_to_float(rbits));
-
-    // Gather 4 scale bytes (lanes 8m, 8m+2, 8m+4, 8m+6) and 4 rope bytes (lanes 4m..4m+3).
-    const uint32_t s1 = __shfl_down(sbyte, 2), s2 = __shfl_down(sbyte, 4), s3 = __shfl_down(sbyte, 6);
-    const uint32_t r1 = __shfl_down(rbyte, 1), r2 = __shfl_down(rbyte, 2), r3 = __shfl_down(rbyte, 3);
-
-    uint8_t* dst = cache + off;
-    ((uint32_t*)dst)[lane] = codes;
-    if ((lane & 7) == 0)
-      ((uint32_t*)(dst + kScaleOff))[lane >> 3] = sbyte | (s1 << 8) | (s2 << 16) | (s3 << 24);
-    if ((lane & 3) == 0)
-      ((uint32_t*)(dst + kRopeOff))[lane >> 2] = rbyte | (r1 << 8) | (r2 << 16) | (r3 << 24);
+      // Words of bytes 256..351: scale dword k (groups 4k..4k+3) is built on lane 4k of the
+      // half, rope dword k (elements 4k..4k+3) on lane 4k (k < 8) or 4(k - 8) (k >= 8).
+      const uint32_t sword = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
+                             (__shfl_down(sbyte, 3) << 24);
+      const uint32_t rwa = rba | (__shfl_down(rba, 1) << 8) | (__shfl_down(rba, 2) << 16) |
+                           (__shfl_down(rba, 3) << 24);
+      const uint32_t rwb = rbb | (__shfl_down(rbb, 1) << 8) | (__shfl_down(rbb, 2) << 16) |
+                           (__shfl_down(rbb, 3) << 24);
+      const int src = (lane & 32) | (4 * (lane & 7));
+      const uint32_t w_s = __shfl(sword, src), w_a = __shfl(rwa, src), w_b = __shfl(rwb, src);
+      if (write) {
+        uint8_t* dst = cache + off;
+        *(uint2v*)(dst + 8 * g) = uint2v{c0, c1};                  // bytes 0..255: codes
+        if (g < 24)                                                 // bytes 256..351
+          ((uint32_t*)(dst + kScaleOff))[g] = g < 8 ? w_s : (g < 16 ? w_a : w_b);
+      }
+    }
   }
 }
 
@@ -102,10 +145,11 @@ hipError_t launch_quantize_append(const void* latent, int64_t latent_stride, con
                                   int64_t rope_stride, const int64_t* slots, int64_t n_rows,
                                   void* cache, int64_t page_stride, int64_t cache_bytes,
                                   hipStream_t stream) {
-  const int64_t waves = n_rows;
+  const int64_t waves = (n_rows + kAppendRowsPerIter - 1) / kAppendRowsPerIter;
   int64_t blocks = (waves + 3) / 4;
-  const int64_t max_blocks = 256 * 32;   // grid-stride beyond 32 blocks per compute unit
+  const int64_t max_blocks = 256 * 256;  // grid-stride beyond 256 blocks per compute unit
   if (blocks > max_blocks) blocks = max_blocks;
+  blocks = (blocks + 7) & ~(int64_t)7;   // a multiple of 8: the same count on every XCD
   hipLaunchKernelGGL(quantize_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
                      slots, n_rows, (uint8_t*)cache, page_stride, cache_bytes);

@@ -10,7 +10,8 @@
 //   * E4M3 encode rounds the fp32 mantissa to 3 bits with round-half-even on the raw bits;
 //   * E2M1 encode compares |x| against the midpoints of the E2M1 grid times the scale
 //     (.25s .75s 1.25s 1.75s 2.5s 3.5s 5s), which are exact fp32 products, with the comparison
-//     sense at each midpoint chosen so that ties go to the even code.
+//     sense at each midpoint chosen so that ties go to the even code; three comparisons (a
+//     binary search over the seven midpoints) give the 3-bit magnitude.
 // Decoding to FP16 MFMA operands uses the gfx950 packed conversions with unit scale, then one
 // packed FP16 multiply by the group scale; every product e2m1 * e4m3 is exact in FP16
 // (at most 6 significant bits, magnitudes in [2^-10, 2688]).
@@ -63,6 +64,21 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return code | sign;
 }
 
+// The same encoding by the gfx950 FP8 conversion, which rounds to nearest even (OCP E4M3);
+// clamping to +-448 first makes every finite value saturate to 0x7E / 0xFE like e4m3_encode.
+// Two values per call: x0 -> byte 0, x1 -> byte 1. Checked against the oracle codec on the GPU
+// for every finite bf16 value and every group scale the encoder can produce.
+__device__ __forceinline__ uint32_t e4m3_encode2_hw(float x0, float x1) {
+  const float c0 = __builtin_amdgcn_fmed3f(x0, -448.0f, 448.0f);
+  const float c1 = __builtin_amdgcn_fmed3f(x1, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
+}
+
+// Value of E4M3 byte 0 of w by the gfx950 conversion (exact).
+__device__ __forceinline__ float e4m3_to_float_hw(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+}
+
 // Value of an E4M3 byte (finite codes).
 __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
@@ -71,14 +87,33 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
-// 4-bit E2M1 code of x against a decoded scale s >= 0 (s == 0: magnitude 0, sign kept).
-__device__ __forceinline__ uint32_t e2m1_encode(float x, float s) {
+// Midpoints of the E2M1 grid times a decoded scale s (.25s .75s 1.25s 1.75s 2.5s 3.5s 5s, exact
+// fp32 products). A zero scale only occurs for groups whose amax is below 6 * 2^-10; their
+// midpoints are set to 2^16, so every element of the group takes magnitude 0.
+struct E2m1Midpoints {
+  float m0, m1, m2, m3, m4, m5, m6;      // named scalars: the search selects between them
+};
+
+__device__ __forceinline__ E2m1Midpoints e2m1_midpoints(float s) {
+  const bool z = !(s > 0.0f);
+  return E2m1Midpoints{z ? 65536.0f : 0.25f * s, z ? 65536.0f : 0.75f * s, z ? 65536.0f : 1.25f * s,
+                       z ? 65536.0f : 1.75f * s, z ? 65536.0f : 2.5f * s,  z ? 65536.0f : 3.5f * s,
+                       z ? 65536.0f : 5.0f * s};
+}
+
+// 4-bit E2M1 code of x (sign kept) against the midpoints of its group, by a search: the
+// comparison with 1.75s picks the lower or upper half of the grid, whose three midpoints then
+// give the remaining two bits. Ties go to the even code, so the comparisons at .75s, 1.75s and
+// 3.5s include equality and those at .25s, 1.25s, 2.5s and 5s do not.
+__device__ __forceinline__ uint32_t e2m1_encode(float x, const E2m1Midpoints& t) {
   const float a = __builtin_fabsf(x);
-  uint32_t mag = (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) +
-                 (uint32_t)(a > 1.25f * s) + (uint32_t)(a >= 1.75f * s) +
-                 (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) + (uint32_t)(a > 5.0f * s);
-  mag = (s > 0.0f) ? mag : 0u;
-  return mag | ((__float_as_uint(x) >> 28) & 8u);
+  const bool hi = a >= t.m3;
+  const float u0 = hi ? t.m4 : t.m0;
+  const float u1 = hi ? t.m5 : t.m1;
+  const float u2 = hi ? t.m6 : t.m2;
+  const bool mid = a >= u1;
+  const bool odd = (mid && a > u2) || (!mid && a > u0);   // both compared: no 4-way table
+  return (uint32_t)hi * 4u + (uint32_t)mid * 2u + (uint32_t)odd + ((__float_as_uint(x) >> 28) & 8u);
 }
 
 // ---- decode to FP16 operands ------------------------------------------------------------------

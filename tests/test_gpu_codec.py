@@ -94,6 +94,24 @@ def test_append_every_bf16_group_max():
              "exhaustive group maxima")
 
 
+def test_append_every_finite_bf16_rope_value():
+    """Every finite bf16 value (both signs, zeros, subnormals, values past the E4M3 range) as a
+    rope element: the rope route of the encoder is checked exhaustively."""
+    print("case: exhaustive bf16 rope values", flush=True)
+    bits = torch.arange(0, 65536, dtype=torch.int32)
+    vals = bits.to(torch.int16).view(torch.bfloat16).float()
+    vals = vals[torch.isfinite(vals)]
+    n_rows = (vals.numel() + 63) // 64
+    rope = torch.cat([vals, torch.zeros(n_rows * 64 - vals.numel())]).reshape(n_rows, 64)
+    g = torch.Generator().manual_seed(13)
+    lat = torch.randn(n_rows, 512, generator=g).bfloat16().cuda()
+    rope = rope.bfloat16().cuda()
+    slots = torch.arange(n_rows, dtype=torch.int64, device="cuda")
+    n_pages = (n_rows + 63) // 64
+    _compare(_run_append(lat, rope, slots, PAGE, n_pages), _expect(lat, rope, slots, PAGE, n_pages),
+             "exhaustive rope values")
+
+
 def test_append_ties_on_grid_midpoints():
     """Elements exactly on E2M1 midpoints for many scales, and rope on E4M3 midpoints."""
     print("case: midpoint ties", flush=True)
