@@ -19,11 +19,11 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_
 
 // Layout: lane l of a wavefront owns group g = l & 31 (16 latent values) of row 2i + (l >> 5),
 // so the per-group work (amax, scale byte, grid midpoints) is done once per group and each half
-// of the wave encodes one row. A wave takes kAppendPairs row pairs per iteration and issues all
-// their loads (slots, latent, rope) before encoding the first, which keeps several rows in flight.
+// of the wave encodes one row. A wave takes PAIRS row pairs per iteration and issues all their
+// loads (slots, latent, rope) before encoding the first, which keeps several rows in flight
+// (PAIRS = 2 for large appends; small appends take one pair per wave, for the shortest latency).
 // The kernel is bound by its integer/compare arithmetic more than by its 1,512 bytes per row.
-constexpr int kAppendPairs = 2;
-constexpr int kAppendRowsPerIter = 2 * kAppendPairs;
+constexpr int64_t kAppendLargeRows = 65536;   // from here on two row pairs per wave
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, l);
@@ -31,6 +31,7 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+template <int PAIRS>
 __global__ __launch_bounds__(256) void quantize_append_kernel(
     const uint16_t* __restrict__ latent, int64_t latent_stride,
     const uint16_t* __restrict__ rope, int64_t rope_stride,
@@ -38,20 +39,21 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
     uint8_t* __restrict__ cache, int64_t page_stride, int64_t cache_bytes) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, g = lane & 31;
-  const int64_t n_iters = (n_rows + kAppendRowsPerIter - 1) / kAppendRowsPerIter;
+  constexpr int kRowsPerIter = 2 * PAIRS;
+  const int64_t n_iters = (n_rows + kRowsPerIter - 1) / kRowsPerIter;
   const int64_t wave_stride = (int64_t)gridDim.x * 4;
   // Workgroup b runs on XCD b % 8 (the grid is a multiple of 8). Consecutive rows are given to
   // workgroups of one XCD, so the rows of a page, whose 352-byte rows share 128-byte lines, are
   // written through one L2.
   const int64_t wg = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   for (int64_t it = wg * 4 + (threadIdx.x >> 6); it < n_iters; it += wave_stride) {
-    const int64_t row0 = it * kAppendRowsPerIter;
+    const int64_t row0 = it * kRowsPerIter;
     // Branch-free loads: rows past the end re-read the last row and are not written.
-    const int64_t slot_l = slots[min(row0 + min(lane, kAppendRowsPerIter - 1), n_rows - 1)];
-    uint4v xa[kAppendPairs], xb[kAppendPairs];
-    uint32_t ra[kAppendPairs], rb[kAppendPairs];
+    const int64_t slot_l = slots[min(row0 + min(lane, kRowsPerIter - 1), n_rows - 1)];
+    uint4v xa[PAIRS], xb[PAIRS];
+    uint32_t ra[PAIRS], rb[PAIRS];
 #pragma unroll
-    for (int p = 0; p < kAppendPairs; ++p) {
+    for (int p = 0; p < PAIRS; ++p) {
       const int64_t row = min(row0 + 2 * p + half, n_rows - 1);
       const uint16_t* lrow = latent + row * latent_stride + 16 * g;
       xa[p] = *(const uint4v*)lrow;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
       rb[p] = rope[row * rope_stride + 32 + g];          // rope element 32 + g
     }
 #pragma unroll
-    for (int p = 0; p < kAppendPairs; ++p) {
+    for (int p = 0; p < PAIRS; ++p) {
       const int64_t row = row0 + 2 * p + half;
       const int64_t slot = half ? readlane64(slot_l, 2 * p + 1) : readlane64(slot_l, 2 * p);
       const int64_t off = (slot / kPageRows) * page_stride + (slot % kPageRows) * kRowBytes;
@@ -145,14 +147,21 @@ hipError_t launch_quantize_append(const void* latent, int64_t latent_stride, con
                                   int64_t rope_stride, const int64_t* slots, int64_t n_rows,
                                   void* cache, int64_t page_stride, int64_t cache_bytes,
                                   hipStream_t stream) {
-  const int64_t waves = (n_rows + kAppendRowsPerIter - 1) / kAppendRowsPerIter;
+  const bool large = n_rows >= kAppendLargeRows;
+  const int64_t rows_per_wave = large ? 4 : 2;
+  const int64_t waves = (n_rows + rows_per_wave - 1) / rows_per_wave;
   int64_t blocks = (waves + 3) / 4;
   const int64_t max_blocks = 256 * 256;  // grid-stride beyond 256 blocks per compute unit
   if (blocks > max_blocks) blocks = max_blocks;
   blocks = (blocks + 7) & ~(int64_t)7;   // a multiple of 8: the same count on every XCD
-  hipLaunchKernelGGL(quantize_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
-                     slots, n_rows, (uint8_t*)cache, page_stride, cache_bytes);
+  if (large)
+    hipLaunchKernelGGL(quantize_append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
+                       slots, n_rows, (uint8_t*)cache, page_stride, cache_bytes);
+  else
+    hipLaunchKernelGGL(quantize_append_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
+                       slots, n_rows, (uint8_t*)cache, page_stride, cache_bytes);
   return hipGetLastError();
 }
 

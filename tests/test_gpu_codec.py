@@ -57,6 +57,22 @@ def test_append_random_rows_bit_exact():
              "random rows")
 
 
+def test_append_large_launch_bit_exact():
+    """A launch past 65,536 rows (two row pairs per wavefront) with a ragged tail, random slots,
+    a few -1 slots and magnitudes spread over the scale range."""
+    print("case: 65,573-row append (large-launch path)", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    n = 65536 + 37
+    mag = torch.exp2(torch.randint(-12, 10, (n, 1), generator=g, device="cuda").float())
+    lat = (torch.randn(n, 512, generator=g, device="cuda") * mag).bfloat16()
+    rope = (torch.randn(n, 64, generator=g, device="cuda") * mag).bfloat16()
+    n_pages = (n + 63) // 64 + 3
+    slots = torch.randperm(n_pages * 64, generator=g, device="cuda")[:n].to(torch.int64)
+    slots[::997] = -1
+    _compare(_run_append(lat, rope, slots, PAGE, n_pages), _expect(lat, rope, slots, PAGE, n_pages),
+             "large launch")
+
+
 def test_append_handworked_golden_row():
     print("case: hand-worked golden row", flush=True)
     from tests.test_oracle_codec import golden_row
