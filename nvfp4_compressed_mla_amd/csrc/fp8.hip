@@ -9,8 +9,9 @@
 // fused decode kernel instantiated for 576-byte rows.
 //
 // Both passes are streaming (HBM-bound) and bit-exact by construction:
-//  * append: every bf16 value -> nearest E4M3, ties to even, saturating at 448 (integer rounding
-//    of the fp32 bits);
+//  * append: every bf16 value -> nearest E4M3, ties to even, saturating at 448 (the gfx950 FP8
+//    conversion after a clamp to +-448, bit-exact with the integer rounding of the fp32 bits for
+//    every bf16 input);
 //  * staging: an NVFP4 value is an E2M1 magnitude (8 choices) times its group's E4M3 scale, so
 //    its E4M3 rounding depends only on (scale byte, magnitude). Each workgroup first tabulates
 //    those 128 x 8 bytes in LDS (the products are exact in fp32), after which a row costs one
@@ -42,12 +43,10 @@ __global__ __launch_bounds__(256) void fp8_append_kernel(
     const uint32_t rbits = rope[row * rope_stride + lane];
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = e4m3_encode(__uint_as_float(x8[i] << 16));
-      const uint32_t hi = e4m3_encode(__uint_as_float(x8[i] & 0xFFFF0000u));
-      w[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-    }
-    const uint32_t rbyte = e4m3_encode(__uint_as_float(rbits << 16));
+    for (int i = 0; i < 4; ++i)
+      w[i >> 1] |= e4m3_encode2_hw(__uint_as_float(x8[i] << 16), __uint_as_float(x8[i] & 0xFFFF0000u))
+                   << (16 * (i & 1));
+    const uint32_t rbyte = e4m3_encode2_hw(__uint_as_float(rbits << 16), 0.0f) & 0xFFu;
     const uint32_t r1 = __shfl_down(rbyte, 1), r2 = __shfl_down(rbyte, 2), r3 = __shfl_down(rbyte, 3);
 
     uint8_t* dst = cache + off;

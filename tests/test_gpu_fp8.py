@@ -49,6 +49,34 @@ def test_fp8_append_bit_exact():
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
 
 
+def test_fp8_append_every_finite_bf16_value():
+    """Every finite bf16 value as a latent element and as a rope element (exhaustive)."""
+    print("case: fp8 append, exhaustive bf16 values", flush=True)
+    m = _m()
+    bits = torch.arange(0, 65536, dtype=torch.int32)
+    vals = bits.to(torch.int16).view(torch.bfloat16).float()
+    vals = vals[torch.isfinite(vals)]
+    n_lat = (vals.numel() + 511) // 512
+    n_rope = (vals.numel() + 63) // 64
+    N = max(n_lat, n_rope)
+    lat = torch.zeros(N * 512)
+    lat[:vals.numel()] = vals
+    rope = torch.zeros(N * 64)
+    rope[:vals.numel()] = vals
+    lat, rope = lat.reshape(N, 512).bfloat16(), rope.reshape(N, 64).bfloat16()
+    page = th.FP8_PAGE_BYTES
+    n_pages = (N + 63) // 64
+    slots = torch.arange(N, dtype=torch.int64)
+    cache = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    m.mla_fp8_append(lat.cuda(), rope.cuda(), slots.cuda(), cache, page)
+    torch.cuda.synchronize()
+    want = np.zeros(n_pages * page, dtype=np.uint8)
+    oc.write_rows(want, page, slots.numpy(), f8.quantize_rows_fp8(lat.double().numpy(), rope.double().numpy()))
+    got = cache.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
 def _random_nvfp4_cache(n_pages, seed):
     """Uniform random bytes with the E4M3 NaN codes (0x7F, 0xFF) replaced in the scale and rope
     parts: every scale value and sign, every code."""
