@@ -83,13 +83,13 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
       // amax * fl(1/6) rounds to the same E4M3 byte as the exact quotient amax / 6 for every
       // finite bf16 amax (checked exhaustively on the host), at the cost of one multiply.
       const uint32_t sbyte = e4m3_encode2_hw(amax * (1.0f / 6.0f), 0.0f) & 0xFFu;
-      const E2m1Midpoints mid = e2m1_midpoints(e4m3_to_float_hw(sbyte));
-      uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        c0 |= e2m1_encode(v[i], mid) << (4 * i);
-        c1 |= e2m1_encode(v[8 + i], mid) << (4 * i);
-      }
+      const float sc = e4m3_to_float_hw(sbyte);
+      const float rinv = sc > 0.0f ? 1.0f / sc : 0.0f;          // IEEE division, once per group
+      const float bound = 8.0f * fmaxf(sc, 0x1p-20f);
+      const float (&va)[8] = *reinterpret_cast<const float(*)[8]>(&v[0]);
+      const float (&vb)[8] = *reinterpret_cast<const float(*)[8]>(&v[8]);
+      const uint32_t c0 = e2m1_encode8_hw(va, sc, rinv, bound);
+      const uint32_t c1 = e2m1_encode8_hw(vb, sc, rinv, bound);
       const uint32_t rpair = e4m3_encode2_hw(bf16_bits_to_float(ra[p]), bf16_bits_to_float(rb[p]));
       const uint32_t rba = rpair & 0xFFu, rbb = rpair >> 8;
 

@@ -6,12 +6,13 @@
 // for low-latency decode": 4-bit latent values with one FP8 scale per 16 values plus a 64-value
 // FP8 rope part, 352 bytes per row.
 //
-// Encoding is integer/compare arithmetic only, so it is bit-exact by construction:
-//   * E4M3 encode rounds the fp32 mantissa to 3 bits with round-half-even on the raw bits;
-//   * E2M1 encode compares |x| against the midpoints of the E2M1 grid times the scale
-//     (.25s .75s 1.25s 1.75s 2.5s 3.5s 5s), which are exact fp32 products, with the comparison
-//     sense at each midpoint chosen so that ties go to the even code; three comparisons (a
-//     binary search over the seven midpoints) give the 3-bit magnitude.
+// Encoding is bit-exact with the format's round-to-nearest-even definition:
+//   * E4M3: e4m3_encode rounds the fp32 mantissa to 3 bits with round-half-even on the raw bits
+//     (integer arithmetic); e4m3_encode2_hw takes the gfx950 FP8 conversion after a clamp to
+//     +-448, which gives the same bytes for every bf16 input;
+//   * E2M1: the quotient x / s goes to the gfx950 FP4 conversion (nearest, ties to even,
+//     saturating); the quotient is corrected with an exact fma residual so that it is exact
+//     whenever x lies on a midpoint of the grid times the scale (see e2m1_encode8_hw).
 // Decoding to FP16 MFMA operands uses the gfx950 packed conversions with unit scale, then one
 // packed FP16 multiply by the group scale; every product e2m1 * e4m3 is exact in FP16
 // (at most 6 significant bits, magnitudes in [2^-10, 2688]).
@@ -87,33 +88,34 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
-// Midpoints of the E2M1 grid times a decoded scale s (.25s .75s 1.25s 1.75s 2.5s 3.5s 5s, exact
-// fp32 products). A zero scale only occurs for groups whose amax is below 6 * 2^-10; their
-// midpoints are set to 2^16, so every element of the group takes magnitude 0.
-struct E2m1Midpoints {
-  float m0, m1, m2, m3, m4, m5, m6;      // named scalars: the search selects between them
-};
-
-__device__ __forceinline__ E2m1Midpoints e2m1_midpoints(float s) {
-  const bool z = !(s > 0.0f);
-  return E2m1Midpoints{z ? 65536.0f : 0.25f * s, z ? 65536.0f : 0.75f * s, z ? 65536.0f : 1.25f * s,
-                       z ? 65536.0f : 1.75f * s, z ? 65536.0f : 2.5f * s,  z ? 65536.0f : 3.5f * s,
-                       z ? 65536.0f : 5.0f * s};
-}
-
-// 4-bit E2M1 code of x (sign kept) against the midpoints of its group, by a search: the
-// comparison with 1.75s picks the lower or upper half of the grid, whose three midpoints then
-// give the remaining two bits. Ties go to the even code, so the comparisons at .75s, 1.75s and
-// 3.5s include equality and those at .25s, 1.25s, 2.5s and 5s do not.
-__device__ __forceinline__ uint32_t e2m1_encode(float x, const E2m1Midpoints& t) {
-  const float a = __builtin_fabsf(x);
-  const bool hi = a >= t.m3;
-  const float u0 = hi ? t.m4 : t.m0;
-  const float u1 = hi ? t.m5 : t.m1;
-  const float u2 = hi ? t.m6 : t.m2;
-  const bool mid = a >= u1;
-  const bool odd = (mid && a > u2) || (!mid && a > u0);   // both compared: no 4-way table
-  return (uint32_t)hi * 4u + (uint32_t)mid * 2u + (uint32_t)odd + ((__float_as_uint(x) >> 28) & 8u);
+// Eight E2M1 codes (element order, low nibble first) of x[0..7] against a decoded group scale s
+// via the gfx950 FP4 conversion, which rounds to nearest even and saturates at 6 (checked
+// against the E2M1 definition, signed zeros included). Its input is the quotient x / s, made exact
+// wherever the rounding decision needs it:
+//   q0 = x * r with r = fl(1/s); e = fma(-q0, s, x) is the exact residual (s has 4 significant
+//   bits); q1 = fma(e, r, q0) is x / s to within a tiny fraction of an ulp.
+// When x lies exactly on a midpoint t*s of the grid (t = .25 .75 1.25 1.75 2.5 3.5 5), q1 == t
+// exactly and the conversion's ties-to-even gives the even code; any other bf16 x is at least
+// 2^-10 away from every midpoint in units of s, far beyond the error of q1. x is first clamped to
+// +-8s (anything past 6s encodes to 6 anyway) so that the products stay finite. A zero scale
+// (s = 0, r = 0) gives signed zeros, i.e. magnitude 0 with the element's sign; the quotient
+// takes the sign of x explicitly (for x = -0 the residual is +0 and the last fma returns +0).
+__device__ __forceinline__ uint32_t e2m1_encode8_hw(const float (&x)[8], float s, float r, float bound) {
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xc = __builtin_amdgcn_fmed3f(x[i], -bound, bound);
+    const float q0 = xc * r;
+    const float e = __builtin_fmaf(-q0, s, xc);
+    // the element's sign, also for x = -0, where the two fmas would return +0
+    q[i] = __builtin_copysignf(__builtin_fmaf(e, r, q0), xc);
+  }
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+  return w;
 }
 
 // ---- decode to FP16 operands ------------------------------------------------------------------
