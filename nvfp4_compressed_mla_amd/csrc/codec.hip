@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "mla_internal.h"
+#include "codec_device.h"
 #include "nvfp4_device.h"
 
 namespace mla {
