@@ -575,7 +575,7 @@ def main():
                 "append_ms": round(ms_app, 4),
                 "append_GBps": round(app_bytes / (ms_app * 1e-3) / 1e9, 1),
                 "append_hbm_frac": round(app_bytes / (ms_app * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                "append_bound": "alu: the VALU issue of the integer/compare encode, not HBM, bounds the launch",
+                "append_bound": "hbm (its VALU issue floor is about the same as the HBM floor)",
                 "decode": run_config(mw, 16, 4, 12),
             }
             del mw
