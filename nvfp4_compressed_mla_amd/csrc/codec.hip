@@ -87,10 +87,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
       const float sc = e4m3_to_float_hw(sbyte);
       const float rinv = sc > 0.0f ? 1.0f / sc : 0.0f;          // IEEE division, once per group
       const float bound = 8.0f * fmaxf(sc, 0x1p-20f);
-      const float (&va)[8] = *reinterpret_cast<const float(*)[8]>(&v[0]);
-      const float (&vb)[8] = *reinterpret_cast<const float(*)[8]>(&v[8]);
-      const uint32_t c0 = e2m1_encode8_hw(va, sc, rinv, bound);
-      const uint32_t c1 = e2m1_encode8_hw(vb, sc, rinv, bound);
+      const uint32_t c0 = e2m1_encode8_hw(v, sc, rinv, bound);        // elements 0..7
+      const uint32_t c1 = e2m1_encode8_hw(v + 8, sc, rinv, bound);    // elements 8..15
       const uint32_t rpair = e4m3_encode2_hw(bf16_bits_to_float(ra[p]), bf16_bits_to_float(rb[p]));
       const uint32_t rba = rpair & 0xFFu, rbb = rpair >> 8;
 

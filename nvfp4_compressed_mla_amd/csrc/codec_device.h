@@ -75,7 +75,7 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
 // +-8s (anything past 6s encodes to 6 anyway) so that the products stay finite. A zero scale
 // (s = 0, r = 0) gives signed zeros, i.e. magnitude 0 with the element's sign; the quotient
 // takes the sign of x explicitly (for x = -0 the residual is +0 and the last fma returns +0).
-__device__ __forceinline__ uint32_t e2m1_encode8_hw(const float (&x)[8], float s, float r, float bound) {
+__device__ __forceinline__ uint32_t e2m1_encode8_hw(const float* x, float s, float r, float bound) {
   float q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
