@@ -345,6 +345,34 @@ def kv_transfer(dev, n_layers=64, ctx=204800, pool_blocks=16000, reps=5):
     return res
 
 
+# ---- measured streaming ceilings ---------------------------------------------------------------
+
+def stream_ceiling(dev, gib=2, reps=5):
+    """HBM rates a plain streaming kernel reaches on this machine, as context for the roofline: a
+    read-only pass (torch's sum over a 2 GiB fp32 tensor) and a device copy of 2 GiB (read + write).
+    Best of `reps` event-timed launches each."""
+    import torch
+    n = gib << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, moved in (("read_sum", lambda: x.sum(), n), ("copy_read_plus_write", lambda: y.copy_(x), 2 * n)):
+        fn()
+        best = None
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1])
+            best = ms if best is None else min(best, ms)
+        out[name] = {"bytes": moved, "ms": round(best, 4), "GBps": round(moved / (best * 1e-3) / 1e9, 1)}
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---- CPU oracle baseline -----------------------------------------------------------------------
 
 def cpu_baseline(wk, budget_s=12.0):
@@ -428,7 +456,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way, mtp_overlap, kv_transfer, topk (default all; 'none' = --no-extra)")
+                         "mixed, three_way, mtp_overlap, kv_transfer, topk, ceiling (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -520,7 +548,8 @@ def main():
     }
 
     wanted = set() if args.no_extra or args.extras == "none" else (
-        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk"} if args.extras == "all"
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk",
+         "ceiling"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
         extra = {}
@@ -616,6 +645,14 @@ def main():
             extra["topk_2048"] = topk_bench(dev)
         if "kv_transfer" in wanted:
             extra["kv_transfer_200K"] = kv_transfer(dev)
+        if "ceiling" in wanted:
+            ceil = stream_ceiling(dev)
+            extra["hbm_stream_ceiling"] = ceil
+            # the faster of the two plain streaming passes (torch's reduction reads well below
+            # the copy's rate on this part)
+            best = max(ceil["read_sum"]["GBps"], ceil["copy_read_plus_write"]["GBps"])
+            result["roofline"]["measured_stream_ceiling_GBps"] = best
+            result["roofline"]["frac_of_measured_stream_ceiling"] = round(achieved / best, 4)
         result["extra"] = extra
 
     if not args.no_cpu_baseline:
