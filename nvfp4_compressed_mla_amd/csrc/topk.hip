@@ -276,11 +276,13 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   // and stays in flight while the cut is found
   const int64_t seg_len = slice / kSegsPerSlice;
   const int64_t p_begin = (int64_t)g * slice + w * seg_len;
+  // Branch-free loads: positions at or past `lim` re-read entry lim - 1 (lim >= 1); their values
+  // are never selected, since the selection tests the position against the row's end.
   auto load_batch = [&](int64_t b0, int64_t lim, float (&v)[kFilterUnroll]) {
 #pragma unroll
     for (int j = 0; j < kFilterUnroll; ++j) {
       const int64_t p = b0 + j * 64 + lane;
-      v[j] = (p < lim) ? row[p] : 0.0f;
+      v[j] = row[min(p, lim - 1)];
     }
   };
   float cur[kFilterUnroll];
@@ -305,13 +307,11 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   uint32_t* ck = cand_key + seg * cap_seg;
   int32_t* cp = cand_pos + seg * cap_seg;
   int cnt = 0;
-  for (int64_t b0 = p_begin; b0 < p_end; b0 += 64 * kFilterUnroll) {
-    float nxt[kFilterUnroll];
-    if (b0 + 64 * kFilterUnroll < p_end) load_batch(b0 + 64 * kFilterUnroll, p_end, nxt);   // next batch in flight
+  auto take_batch = [&](int64_t b0, const float (&v)[kFilterUnroll]) {
 #pragma unroll
     for (int j = 0; j < kFilterUnroll; ++j) {
       const int64_t p = b0 + j * 64 + lane;
-      const uint32_t key = score_key(cur[j]);
+      const uint32_t key = score_key(v[j]);
       const bool sel = p < p_end && key >= cut;
       const uint64_t mask = __ballot(sel);
       if (sel) {
@@ -321,8 +321,17 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
       }
       cnt += __popcll(mask);
     }
-#pragma unroll
-    for (int j = 0; j < kFilterUnroll; ++j) cur[j] = nxt[j];
+  };
+  // Two register buffers used in turn (no copy between them, which would wait for the batch
+  // just issued): while one batch is taken, the next one is in flight.
+  constexpr int64_t kBatch = 64 * kFilterUnroll;
+  float nxt[kFilterUnroll];
+  for (int64_t b0 = p_begin; b0 < p_end; b0 += 2 * kBatch) {
+    if (b0 + kBatch < p_end) load_batch(b0 + kBatch, p_end, nxt);
+    take_batch(b0, cur);
+    if (b0 + kBatch >= p_end) break;
+    if (b0 + 2 * kBatch < p_end) load_batch(b0 + 2 * kBatch, p_end, cur);
+    take_batch(b0 + kBatch, nxt);
   }
   if (lane == 0) seg_cnt[seg] = cnt;                       // the true count, even past cap_seg
 }
