@@ -140,6 +140,7 @@ __device__ __forceinline__ half4v lds_tr16(const uint8_t* p) {
 }
 
 constexpr int kDecSlots = 3;
+constexpr int kStreamPartialSplits = 8;                       // see the epilogue
 constexpr int kProducers = 8;                                 // producer waves (2 per SIMD)
 
 // FP8 selects 576-byte FP8 rows (the baseline format): they need no group scales, so the
@@ -622,12 +623,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int n = 0; n < 4; ++n) dst[16 * n] = o[hb][n][e] * inv[e];
         }
       } else {
-        // FP16 partial in register order: [token][split][16-head block][dim block][lane][4 heads]
+        // FP16 partial in register order: [token][split][16-head block][dim block][lane][4 heads].
+        // With at most kStreamPartialSplits splits the partials are written with streaming
+        // (non-temporal) stores: they then leave no dirty lines for the end-of-kernel L2
+        // write-back, which shortens this kernel by more than the combine, whose single round of
+        // loads then reads them from the memory-side cache, loses. With more splits the combine
+        // reads in several rounds and the partials are better kept in the L2.
         _Float16* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+        const bool stream = a.n_split <= kStreamPartialSplits;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const float4v v = o[hb][n] * inv;
-          *(half4v*)(dst + 256 * n) = half4v{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          const half4v hv = half4v{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          if (stream)
+            __builtin_nontemporal_store(__builtin_bit_cast(uint2v, hv), (uint2v*)(dst + 256 * n));
+          else
+            *(half4v*)(dst + 256 * n) = hv;
         }
       }
       if (pw == 0 && l16 == 0) {
