@@ -345,6 +345,35 @@ def kv_transfer(dev, n_layers=64, ctx=204800, pool_blocks=16000, reps=5):
     return res
 
 
+# ---- cache-flush cross-check -------------------------------------------------------------------
+
+def flush_check(wk, launches=24):
+    """The fused kernel timed with a 1 GiB scratch fill before every launch, which evicts the L2s
+    and the 256 MB Infinity Cache, as a cross-check of the rotated-input timing (the rotation is
+    what keeps the timed steps from being served by those caches)."""
+    import torch
+    import nvfp4_compressed_mla_amd as m
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=wk.out.device)
+    durs = []
+    for i in range(launches + 4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        scratch.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        m.mla_set_timing_events(a.cuda_event, b.cuda_event)
+        try:
+            wk.decode(i % wk.rot)
+        finally:
+            m.mla_set_timing_events(None, None)
+        torch.cuda.synchronize()
+        if i >= 4:
+            durs.append(a.elapsed_time(b))
+    del scratch
+    torch.cuda.empty_cache()
+    return sum(durs) / len(durs)
+
+
 # ---- measured streaming ceilings ---------------------------------------------------------------
 
 def stream_ceiling(dev, gib=2, reps=5):
@@ -456,7 +485,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way, mtp_overlap, kv_transfer, topk, ceiling (default all; 'none' = --no-extra)")
+                         "mixed, three_way, mtp_overlap, kv_transfer, topk, ceiling, flush (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -549,7 +578,7 @@ def main():
 
     wanted = set() if args.no_extra or args.extras == "none" else (
         {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk",
-         "ceiling"} if args.extras == "all"
+         "ceiling", "flush"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
         extra = {}
@@ -645,6 +674,13 @@ def main():
             extra["topk_2048"] = topk_bench(dev)
         if "kv_transfer" in wanted:
             extra["kv_transfer_200K"] = kv_transfer(dev)
+        if "flush" in wanted:
+            kf = flush_check(wk)
+            extra["mall_flush_check_batched"] = {
+                "kernel_us_flushed": round(kf * 1e3, 2),
+                "kernel_us_rotated": round(kavg * 1e3, 2),
+                "note": "flushed: a 1 GiB scratch fill before every single launch; rotated: the "
+                        "roofline's eager launches over the 48 rotated input sets"}
         if "ceiling" in wanted:
             ceil = stream_ceiling(dev)
             extra["hbm_stream_ceiling"] = ceil
