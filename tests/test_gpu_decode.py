@@ -167,3 +167,53 @@ def test_overlapping_lists_across_query_tokens():
     for s in (0, 1, 3):
         out, lse = _sparse(case, s)
         th.assert_parity(out, lse, ref_o, ref_l, what=f"overlap 0.8 splits={s}")
+
+
+def test_cache_beyond_4_gib():
+    """A 4.5 GiB cache whose pages all lie past the 4 GiB mark: 64-bit row offsets in the append
+    and in the decode's gathers (sparse and dense). The oracle works on a compact copy of the same
+    rows, which it quantizes itself; the bytes past 4 GiB must equal its rows."""
+    from oracle import attention as oa
+    from oracle import cache as oc
+    from oracle import nvfp4 as nv
+    print("case: 4.5 GiB cache, every page past 4 GiB", flush=True)
+    m = _m()
+    dev = "cuda"
+    page = th.PAGE_BYTES
+    B, q_len, H, topk = 2, 2, 64, 512
+    ctx = [2000, 1500]
+    ppr = [(c + 63) // 64 for c in ctx]
+    n_big = (9 << 29) // page + 1                       # 4.5 GiB of pages
+    base = (1 << 32) // page + 7                        # first page used: past 4 GiB
+    assert (base + sum(ppr)) <= n_big and base * page > (1 << 32)
+    bt_small = torch.full((B, max(ppr)), -1, dtype=torch.int32)
+    first = 0
+    for b in range(B):
+        bt_small[b, :ppr[b]] = torch.arange(first, first + ppr[b], dtype=torch.int32)
+        first += ppr[b]
+    bt_big = torch.where(bt_small >= 0, bt_small + base, bt_small).to(dev)
+    lat, rope = wl.gen_latent_rope(sum(ctx), 61, dev)
+    cache = torch.zeros(n_big * page, dtype=torch.uint8, device=dev)
+    slots = torch.cat([wl.slot_mapping_for(bt_big, b, 0, c) for b, c in enumerate(ctx)])
+    m.mla_nvfp4_quantize_append(lat, rope, slots, cache, page)
+    q = wl.gen_queries(B, q_len, H, "bf16", 62, dev)
+    idx = wl.gen_topk(B, q_len, topk, ctx, 63, dev)
+    seq = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    scale = th.softmax_scale()
+    out, lse = m.mla_sparse_decode(q, cache, page, bt_big, idx, scale)
+    out_d, lse_d = m.mla_dense_decode(q, cache, page, bt_big, seq, scale, split_tokens=1024)
+    torch.cuda.synchronize()
+    got = cache[base * page:(base + sum(ppr)) * page].cpu().numpy()
+    del cache
+    torch.cuda.empty_cache()
+
+    host = np.zeros(sum(ppr) * page, dtype=np.uint8)
+    slots_small = torch.cat([wl.slot_mapping_for(bt_small, b, 0, c) for b, c in enumerate(ctx)]).numpy()
+    oc.write_rows(host, page, slots_small,
+                  nv.quantize_rows(lat.double().cpu().numpy(), rope.double().cpu().numpy()))
+    assert np.array_equal(got, host), "bytes written past 4 GiB differ from the oracle's rows"
+    q64 = q.float().cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oa.sparse_decode(q64, host, page, bt_small.numpy(), idx.cpu().numpy(), scale)
+    th.assert_parity(out, lse, ref_o, ref_l, what="sparse, pages past 4 GiB")
+    ref_od, ref_ld = oa.dense_decode(q64, host, page, bt_small.numpy(), seq.cpu().numpy(), scale)
+    th.assert_parity(out_d, lse_d, ref_od, ref_ld, what="dense, pages past 4 GiB")
