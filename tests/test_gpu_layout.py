@@ -80,3 +80,35 @@ def test_decode_one_layer_of_block_major_pool_after_transfer():
     # the other layers of the destination pool stay untouched
     other = dst.cpu().numpy().reshape(ndst, L, P)
     assert not other[:, [0, 2]].any()
+
+
+@pytest.mark.parametrize("layout", [lo.BLOCK_MAJOR, lo.LAYER_MAJOR])
+def test_copy_blocks_past_4_gib(layout):
+    """64-layer pools of about 4.2 GiB: blocks whose pages lie past the 4 GiB mark are copied
+    (64-bit page offsets); every page of every copied pair is compared at the offsets the oracle's
+    layout gives, and the pages of a block that is not copied stay untouched."""
+    print(f"case: copy_kv_blocks past 4 GiB, layout={layout}", flush=True)
+    m = _m()
+    L, nb = 64, 3100
+    pool = nb * L * P
+    assert pool > (1 << 32)
+    g = torch.Generator(device="cuda").manual_seed(70 + layout)
+    src = torch.randint(0, 256, (pool,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.zeros(pool, dtype=torch.uint8, device="cuda")
+    sb = np.array([3099, 3050, 2990, 17, 3001], dtype=np.int32)
+    db = np.array([3098, 5, 3097, 3090, 2999], dtype=np.int32)
+    m.mla_copy_kv_blocks(src, dst, layout, L, P, torch.from_numpy(sb).cuda(), torch.from_numpy(db).cuda())
+    torch.cuda.synchronize()
+    high = 0
+    for s_blk, d_blk in zip(sb, db):
+        for layer in range(L):
+            so = lo.page_offset(layout, int(s_blk), layer, L, P, nb)
+            do = lo.page_offset(layout, int(d_blk), layer, L, P, nb)
+            high += do + P > (1 << 32)
+            assert torch.equal(dst[do:do + P], src[so:so + P]), f"block {s_blk}->{d_blk} layer {layer}"
+    assert high > 0
+    for layer in (0, 31, 63):
+        o = lo.page_offset(layout, 3096, layer, L, P, nb)      # never a destination
+        assert int(dst[o:o + P].count_nonzero()) == 0
+    del src, dst
+    torch.cuda.empty_cache()
