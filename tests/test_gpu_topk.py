@@ -34,6 +34,8 @@ def _run(scores, seq_lens, q_len, k):
     (16384, 2048, 2, [16385, 2049], True),         # a window of 2048 - 1 + t
     (33000, 512, 1, [33000], True),
     (700, 2048, 1, [700], False),                  # fewer positions than k: -1 padding
+    (1 << 20, 2048, 1, [1 << 20, 700001], False),  # the longest row the entry point accepts
+    (1 << 20, 1, 2, [1 << 20, 1 << 20], True),     # k = 1 among many equal maxima: position order
 ])
 def test_topk_matches_oracle(n_max, k, q_len, seq_lens, ties):
     print(f"case: topk n_max={n_max} k={k} q_len={q_len} seq_lens={seq_lens} ties={ties}", flush=True)
