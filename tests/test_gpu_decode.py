@@ -217,3 +217,32 @@ def test_cache_beyond_4_gib():
     th.assert_parity(out, lse, ref_o, ref_l, what="sparse, pages past 4 GiB")
     ref_od, ref_ld = oa.dense_decode(q64, host, page, bt_small.numpy(), seq.cpu().numpy(), scale)
     th.assert_parity(out_d, lse_d, ref_od, ref_ld, what="dense, pages past 4 GiB")
+
+
+@pytest.mark.parametrize("H", [48, 64])
+def test_fp32_queries_every_head_block(H):
+    """fp32 queries with three and four 16-head blocks per workgroup, sparse and dense."""
+    print(f"case: fp32 queries H={H} k=700 ctx=[1900, 800] q_len=2", flush=True)
+    case = th.build_case(2, 2, H, [1900, 800], 700, seed=300 + H, q_dtype="fp32")
+    ref_o, ref_l = th.oracle_sparse(case)
+    for s in (1, 3):
+        out, lse = _sparse(case, s)
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"fp32 q H={H} splits={s}")
+    ref_od, ref_ld = th.oracle_dense(case)
+    out, lse = _dense(case, 512)
+    th.assert_parity(out, lse, ref_od, ref_ld, what=f"fp32 q dense H={H}")
+
+
+def test_dense_empty_and_tiny_windows():
+    """q_len = 3 over requests of 1, 2, 65 and 130 positions: query token t sees positions
+    0..seq_len-3+t, so the first tokens of the short requests see nothing (output 0, lse -inf),
+    and the others see 1, 2, 63..66 or 128..130 positions."""
+    print("case: dense empty / one-position windows, q_len=3", flush=True)
+    case = th.build_case(4, 3, 64, [1, 2, 65, 130], 0, seed=17)
+    ref_o, ref_l = th.oracle_dense(case)
+    assert np.isneginf(ref_l[0, 0]).all() and np.isneginf(ref_l[0, 1]).all()
+    for st in (64, 4096):
+        out, lse = _dense(case, st)
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"dense tiny windows split_tokens={st}")
+        o = out.cpu().numpy()
+        assert np.all(o[0, 0] == 0) and np.all(o[0, 1] == 0) and np.all(o[1, 0] == 0)
