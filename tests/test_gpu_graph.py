@@ -1,7 +1,9 @@
-"""The hot path captured in a HIP graph, and on two streams at once. Graph: quantize-append, sparse decode with a split combine and
-dense decode recorded once and replayed several times, with eager work and synchronizations
-between the replays. Every replay must reproduce the eager launch bit for bit (the kernels are
-deterministic and the library records no memset or allocation into the graph)."""
+"""The hot path captured in a HIP graph, and run on two streams at once.
+
+Graph: quantize-append, sparse decode with a split combine and dense decode recorded once and
+replayed several times, with eager work and synchronizations between the replays. Every replay
+must reproduce the eager launch bit for bit (the kernels are deterministic and the library
+records no memset or allocation into the graph)."""
 
 import math
 
