@@ -2,8 +2,10 @@
 
 Each case builds the whole cache on the GPU at its real size (140K-200K-token requests, 64-row
 pages, random block tables), runs the decode with the library's own split choice (the one
-bench.py uses), and compares sampled query tokens -- all heads and all 512 output dims of each --
-with the fp64 oracle. The oracle quantizes, by itself, only the bf16 rows those tokens read.
+bench.py uses), and compares query tokens -- all heads and all 512 output dims of each -- with
+the fp64 oracle: every token of the batched configuration, two whole requests plus three tokens
+of the MTP one, sampled tokens of the dense and mixed ones. The oracle quantizes, by itself,
+only the bf16 rows those tokens read.
 """
 
 import numpy as np
@@ -47,7 +49,7 @@ def test_batched_140k_topk2048():
     case = th.build_case(32, 1, 64, [143360] * 32, 2048, seed=1001, spare_pages=0,
                          topk_fn=lambda B, q, k, ctx, s, d: wl.gen_topk_batched(B, q, k, ctx[0], s, d))
     assert _m().mla_sparse_decode_num_splits(32, 64, 2048, 0) == 8
-    _sampled_sparse(case, [(0, 0), (7, 0), (13, 0), (19, 0), (26, 0), (31, 0)], "batched")
+    _sampled_sparse(case, [(b, 0) for b in range(32)], "batched (every output row)")
 
 
 def test_mtp_146k_q15():
@@ -56,7 +58,8 @@ def test_mtp_146k_q15():
     case = th.build_case(16, 15, 64, [149504] * 16, 2048, seed=1002, spare_pages=0,
                          topk_fn=lambda B, q, k, ctx, s, d: wl.gen_topk_batched(B, q, k, ctx[0], s, d),
                          append_rows=6144)
-    _sampled_sparse(case, [(0, 0), (0, 14), (5, 7), (9, 3), (12, 11), (15, 14)], "mtp")
+    tokens = [(b, t) for b in (0, 15) for t in range(15)] + [(5, 7), (9, 3), (12, 11)]
+    _sampled_sparse(case, tokens, "mtp (requests 0 and 15 whole, three more tokens)")
 
 
 def test_dense_146k_split4096():
