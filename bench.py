@@ -404,6 +404,17 @@ def stream_ceiling(dev, gib=2, reps=5):
 
 # ---- CPU oracle baseline -----------------------------------------------------------------------
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wk, budget_s=12.0):
     """The CPU oracle (fp64 NumPy, untuned) on the same step: quantize the step's new rows and
     decode all query tokens of rotation 0 from a cache the oracle built itself from the same bf16
@@ -448,7 +459,8 @@ def cpu_baseline(wk, budget_s=12.0):
         "kind": "oracle",
         "sample": (f"{n} whole step(s) of the batched config ({wk.B * wk.q_len} query tokens x "
                    f"{wk.topk} rows + {wk.append_rows * wk.B} appended rows), "
-                   f"{dt * 1e3:.0f} ms per step; host cpus visible: {len(os.sched_getaffinity(0))}"),
+                   f"{dt * 1e3:.0f} ms per step; host cpus visible: {len(os.sched_getaffinity(0))}; "
+                   f"cpu: {cpu_model()}"),
     }
 
 
