@@ -309,7 +309,11 @@ def _sparse(name, q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax
 def mla_dense_decode(q, kv_cache, page_stride_bytes, block_table, seq_lens, softmax_scale,
                      split_tokens: int = 4096, out=None, lse=None, workspace=None, want_lse=True,
                      stream=None):
-    """Dense decode over positions 0..seq_len-q_len+t; returns (out, lse)."""
+    """Dense decode over positions 0..seq_len-q_len+t; returns (out, lse).
+
+    ``split_tokens``: positions per row split (a multiple of 64); 0 takes the library's split
+    size that keeps the launch in one wave of workgroups (``mla_dense_decode_split_tokens``).
+    """
     return _dense("mla_dense_decode", q, kv_cache, page_stride_bytes, block_table, seq_lens,
                   softmax_scale, split_tokens, out, lse, workspace, want_lse, stream)
 
@@ -336,6 +340,8 @@ def _dense(name, q, kv_cache, page_stride_bytes, block_table, seq_lens, softmax_
         raise ValueError("block_table must be contiguous int32 [B, max_pages]")
     if seq_lens.numel() != B or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be contiguous int32 [B]")
+    if split_tokens == 0:          # the library's one-wave split size for this shape
+        split_tokens = mla_dense_decode_split_tokens(B * q_len, H, block_table.shape[1])
     splits = mla_dense_decode_num_splits(block_table.shape[1], split_tokens)
     out, lse = _outputs(q, out, lse, want_lse)
     workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)

@@ -239,3 +239,4 @@ def test_dense_one_wave_split_helper(lib):
         if st < 8192 and st > 64:
             assert T * groups * ns(P, st) <= 256
     assert f(0, 64, 10) == 4096 and f(4, 8, 10) == 4096
+

@@ -246,3 +246,17 @@ def test_dense_empty_and_tiny_windows():
         th.assert_parity(out, lse, ref_o, ref_l, what=f"dense tiny windows split_tokens={st}")
         o = out.cpu().numpy()
         assert np.all(o[0, 0] == 0) and np.all(o[0, 1] == 0) and np.all(o[1, 0] == 0)
+
+
+def test_dense_split_tokens_zero_is_the_one_wave_size():
+    """split_tokens=0 in the binding takes the library's one-wave split size: the same bits as
+    passing that size, and parity with the oracle."""
+    print("case: dense split_tokens=0", flush=True)
+    m = _m()
+    case = th.build_case(3, 2, 64, [5000, 3100, 800], 0, seed=23)
+    auto = m.mla_dense_decode_split_tokens(6, 64, case.block_table.shape[1])
+    o0, l0 = _dense(case, 0)
+    o1, l1 = _dense(case, auto)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    ref_o, ref_l = th.oracle_dense(case)
+    th.assert_parity(o0, l0, ref_o, ref_l, what="dense split_tokens=0")
