@@ -295,6 +295,44 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   lds_barrier();
   const int n_tiles = (n_rows + kTileRows - 1) / kTileRows;
 
+  // No valid row (an empty list, or a split past the end of the list or of the visible
+  // positions): every wave knows n_rows here, so the workgroup leaves together. The result is the
+  // softmax over no rows, written by the producer waves in the epilogue's layout: zero outputs
+  // and lse = -inf. No query load or gather has been issued yet.
+  if (n_rows == 0) {
+    if (!math) {
+      const bool final_out = (a.n_split == 1);
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb) {
+        const int hbg = (head0 >> 4) + hb;
+        if (final_out) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float* dst = a.out + ((int64_t)tok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) dst[16 * n] = 0.0f;
+          }
+        } else {
+          _Float16* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) *(uint2v*)(dst + 256 * n) = uint2v{0u, 0u};
+        }
+        if (pw == 0 && l16 == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int head = 16 * hbg + 4 * kg + e;
+            if (final_out) {
+              if (a.lse) a.lse[(int64_t)tok * a.H + head] = -INFINITY;
+            } else {
+              a.ws_lse[((int64_t)tok * a.n_split + split) * a.H + head] = -INFINITY;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+
   float* fin_m = (float*)pbuf[0];               // epilogue: per-head running max and sum
   float* fin_l = fin_m + 64;
 

@@ -260,3 +260,42 @@ def test_dense_split_tokens_zero_is_the_one_wave_size():
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     ref_o, ref_l = th.oracle_dense(case)
     th.assert_parity(o0, l0, ref_o, ref_l, what="dense split_tokens=0")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("H", [64, 80])
+def test_empty_tokens_and_empty_splits_write_every_output(fmt, H):
+    """Workgroups with no valid row leave before the tile loop: requests padded with all -1 lists
+    (a mixed step's shorter requests) and tokens whose valid entries all sit in the first split's
+    part of the list, so that the later splits are empty. The output and the split workspace start
+    as NaN bytes: every element must be written, empty tokens give +0 and lse -inf, and the others
+    match the oracle."""
+    print(f"case: empty tokens / empty splits fmt={fmt} H={H}", flush=True)
+    m = _m()
+    B, q_len, k = 4, 5, 1024
+    case = th.build_case(B, q_len, H, [3000, 2500, 1800, 4100], k, seed=900 + H, fmt=fmt)
+    idx = case.topk_idx.clone()
+    q_lens = [5, 1, 2, 5]
+    for b, n in enumerate(q_lens):
+        idx[b, n:] = -1                                    # padding tokens of shorter requests
+    idx[0, 1, 100:] = -1                                   # valid entries only in the first 100
+    idx[3, 2, :] = -1
+    idx[3, 2, 7] = 11                                      # one entry, in the first split
+    case.topk_idx = idx.contiguous()
+    ref_o, ref_l = th.oracle_sparse(case)
+    fn = m.mla_sparse_decode if fmt == "nvfp4" else m.mla_fp8_sparse_decode
+    for s in (1, 4, 16):
+        out = torch.full((B, q_len, H, 512), float("nan"), device="cuda")
+        lse = torch.full((B, q_len, H), float("nan"), device="cuda")
+        ws = torch.full((max(m.mla_decode_workspace_size(B * q_len, H, s), 256),), 0xFF,
+                        dtype=torch.uint8, device="cuda")
+        fn(case.q, case.cache, case.page_stride, case.block_table, case.topk_idx,
+           th.softmax_scale(), out=out, lse=lse, num_splits=s, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any(), f"splits={s}"
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"{fmt} H={H} empty tokens splits={s}")
+        for b, n in enumerate(q_lens):
+            if n < q_len:
+                pad = out[b, n:]
+                assert torch.all(pad == 0) and not torch.signbit(pad).any(), f"splits={s} b={b}"
+                assert torch.all(torch.isneginf(lse[b, n:])), f"splits={s} b={b}"
