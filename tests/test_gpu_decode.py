@@ -299,3 +299,35 @@ def test_empty_tokens_and_empty_splits_write_every_output(fmt, H):
                 pad = out[b, n:]
                 assert torch.all(pad == 0) and not torch.signbit(pad).any(), f"splits={s} b={b}"
                 assert torch.all(torch.isneginf(lse[b, n:])), f"splits={s} b={b}"
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_block_table_width_staged_and_memory_lookups(fmt):
+    """The block table's width is only a stride: padding it with -1 columns (to 9,216 and 9,217
+    entries per row) gives the same bits as the unpadded table. List entries that point into the
+    padding, or beyond the narrow table, are empty entries."""
+    print(f"case: block-table widths 9216 / 9217 fmt={fmt}", flush=True)
+    m = _m()
+    case = th.build_case(3, 2, 64, [3000, 2200, 700], 512, seed=61, fmt=fmt)
+    fn = m.mla_sparse_decode if fmt == "nvfp4" else m.mla_fp8_sparse_decode
+    idx = case.topk_idx.clone()
+    idx[0, 0, 5] = 9000 * 64 + 3                        # page column 9000: padding (-1), skipped
+    idx[1, 1, 9] = 9216 * 64                            # column 9216: only in the wider table
+    idx[2, 0, 0] = 200000                               # beyond the narrow table
+    # the library treats an unmapped page or a position beyond the table as an empty entry
+    case.topk_idx = idx.clone()
+    case.topk_idx[0, 0, 5] = case.topk_idx[1, 1, 9] = case.topk_idx[2, 0, 0] = -1
+    ref_o, ref_l = th.oracle_sparse(case)
+    results = []
+    for width in (case.block_table.shape[1], 9216, 9217):
+        bt = torch.full((3, width), -1, dtype=torch.int32, device="cuda")
+        bt[:, :case.block_table.shape[1]] = case.block_table
+        for s in (1, 4):
+            out, lse = fn(case.q, case.cache, case.page_stride, bt.contiguous(), idx.contiguous(),
+                          th.softmax_scale(), num_splits=s)
+            torch.cuda.synchronize()
+            results.append((width, s, out.clone(), lse.clone()))
+    for width, s, out, lse in results:
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"{fmt} width={width} splits={s}")
+        base = next(r for r in results if r[1] == s)
+        assert torch.equal(out, base[2]) and torch.equal(lse, base[3]), f"width={width} splits={s}"
