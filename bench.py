@@ -13,7 +13,7 @@ Inputs are synthetic and seeded, generated and quantized on the GPU before timin
 HIP graphs. The fused decode kernel's own duration is taken with HIP events recorded around it by
 the library (``mla_set_timing_events``) on the launch stream.
 
-``--gpus N`` with N > 1 exits: this build runs on one GPU.
+``--gpus N`` with N > 1 exits: the library and this benchmark run on one GPU.
 """
 
 from __future__ import annotations
@@ -505,8 +505,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sharding is described in the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; each GPU "
+              "would serve its own requests with no exchange between GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch

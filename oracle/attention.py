@@ -12,16 +12,16 @@ latent KV head is used:
 * for head h: ``s_j = scale * (q_h . K_j)``, ``o_h = sum_j softmax(s)_j V_j``,
   ``lse_h = log sum_j exp(s_j)`` (natural log).
 
-Readings (the page is silent or terse; each is listed in the design notes):
+Readings (the page is silent or terse):
 
-* One index list per query token, shared by all heads ("for each query token ... partition the
-  selected rows").
+* One index list per query token, shared by all heads (the page selects rows per query token
+  and splits that token's rows across blocks).
 * Entry ``-1`` is an empty slot (subsection "Skip loads for empty slots"): it is not loaded and
   contributes no term; an all-empty list yields ``o = 0`` and ``lse = -inf``.
 * Duplicated positions each contribute a term.
 * Dense decode attends to positions ``0..seq_len-1``; with ``q_len > 1`` query token ``t`` sees
   positions ``j <= seq_len - q_len + t``.
-* Splitting a token's rows across blocks and merging ("partial results are merged") leaves the
+* Splitting a token's rows across blocks and merging the blocks' partial results leaves the
   result equal to the unsplit softmax; ``lse_merge`` is that merge written out.
 """
 

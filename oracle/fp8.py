@@ -8,7 +8,7 @@ decode kernel" compares the fused NVFP4 kernel with (a) the existing FP8 attenti
 rows and (b) a staged path that first unpacks the selected NVFP4 rows into a temporary FP8 buffer
 and then runs that FP8 kernel.
 
-Readings taken where the page is silent (each listed in the design notes):
+Readings taken where the page is silent:
 
 * The 576-byte row is bytes [0, 512) = E4M3 of latent element i at byte i, bytes [512, 576) =
   E4M3 of rope element j at byte 512 + j, scale 1 for both (there is no room for scales).

@@ -6,7 +6,7 @@ Row format, [PI] section "Making room for low-latency decode": a cache row holds
 latent as 4-bit values with one FP8 scale per 16 values (512/2 + 512/16 = 288 bytes) and the
 64-value rope part as FP8 (64 bytes): 352 bytes, against 512 + 64 = 576 bytes for an all-FP8 row.
 
-Readings taken where the page is silent (each one is listed with its reason in the design notes):
+Readings taken where the page is silent, each with its reason:
 
 * FP8 is OCP E4M3 (E4M3FN): bias 7, max 448, code 0x7F/0xFF is NaN, no infinities.
 * The 4-bit element is OCP MX FP4 E2M1.
