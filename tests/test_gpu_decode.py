@@ -263,7 +263,7 @@ def test_dense_split_tokens_zero_is_the_one_wave_size():
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-@pytest.mark.parametrize("H", [64, 80])
+@pytest.mark.parametrize("H", [64, 80, 128])
 def test_empty_tokens_and_empty_splits_write_every_output(fmt, H):
     """Workgroups with no valid row leave before the tile loop: requests padded with all -1 lists
     (a mixed step's shorter requests) and tokens whose valid entries all sit in the first split's
