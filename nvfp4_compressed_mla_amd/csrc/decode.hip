@@ -27,7 +27,8 @@
 // Decoded tile layout ("fragment-major"): for row block rb (16 rows) and K-chunk c (32 dims),
 // 1 KB holds 64 slots of 16 bytes; row r, dims 8*dg..8*dg+7 of the chunk sit in slot
 // 16*dg + (r ^ 4*(dg & 1)). QK fragment reads are then whole 1 KB blocks, and the XOR keeps the
-// transposing V reads free of LDS bank conflicts.
+// transposing V reads free of LDS bank conflicts; the QK lanes take the 8-dim groups in the order
+// 0, 2, 1, 3, which keeps their reads conflict-free too (measured per access pattern).
 //
 // Splits write normalised partial outputs (in the producers' register order, 16-byte stores) and
 // their log-sum-exp; combine_kernel merges them in split order (deterministic). With a single
@@ -174,7 +175,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   // ---- queries of head block w (math waves) -------------------------------------------------
   const bool qk_wave = math && w < NH;
-  const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kg;
+  // QK lane block kg carries 8-dim group kdg of each 32-dim chunk (groups 0, 2, 1, 3): the
+  // decoded-tile slots of odd groups are XOR-swizzled for the transposing V reads, and with this
+  // order lanes 0-31 read unswizzled slots and lanes 32-63 swizzled ones, which keeps the QK
+  // fragment reads free of LDS bank conflicts (with kdg = kg every such read was 2-way). The
+  // queries follow the same order, so the contraction is unchanged.
+  const int kdg = ((kg & 1) << 1) | (kg >> 1);
+  const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kdg;
   half8v qf[kChunks];                         // queries as 18 FP16 fragments (math waves)
   // Loaded after the index compaction (their traffic would otherwise slow its dependent loads
   // down), while the producers' first gathers are in flight; converted to FP16 (softmax_scale *
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     uint32_t next_o16[3] = {kInvalid, kInvalid, kInvalid};   // row offsets of the next tile to gather
     if constexpr (!FP8) tile_offsets(3, next_o16);
     float m_run = -INFINITY, l_run = 0.0f;     // running max (log2 units), partial sum
-    const int kslot = ((kg << 4) + (l16 ^ ((kg & 1) << 2))) << 4;   // QK A-fragment slot
+    const int kslot = ((kdg << 4) + (l16 ^ ((kdg & 1) << 2))) << 4;   // QK A-fragment slot
     // One loop per kind of math wave (head-block owners and, when a group has fewer than four
     // head blocks, gather-only waves), so that neither carries the other's registers.
     auto math_loop = [&](auto qkw_tag) {
