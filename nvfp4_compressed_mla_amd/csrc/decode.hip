@@ -56,7 +56,11 @@ constexpr int kRawSlots = 3;
 constexpr int kChunks = kQkDim / 32;                          // 18 K-chunks of 32 dims
 constexpr int kFragBytes = 1024;                              // one 16 x 32 FP16 fragment
 constexpr int kDecTileBytes = 2 * kChunks * kFragBytes;       // 36864
-constexpr int kPStride = 80;                                  // bytes per head row of P
+constexpr int kPStride = 64;                                  // bytes per head row of P
+// P row h holds the tile's 32 probabilities of one head; its four 16-byte columns (8 rows each)
+// are stored at column c ^ ((h >> 1) & 3), which keeps the PV reads of P free of LDS bank
+// conflicts (measured per access pattern).
+__device__ __forceinline__ int p_col(int h, int c) { return 16 * (c ^ ((h >> 1) & 3)); }
 constexpr int kThreads = 768;
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 
@@ -471,9 +475,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           }
           l_run = l_run * alpha + psum;
           m_run = m_new;
-          uint8_t* prow_p = pbuf[i & 1] + (16 * w + l16) * kPStride;
-          *(half4v*)(prow_p + 8 * kg) = pf[0];           // rows 4kg..4kg+3
-          *(half4v*)(prow_p + 32 + 8 * kg) = pf[1];      // rows 16+4kg..
+          const int ph = 16 * w + l16;
+          uint8_t* prow_p = pbuf[i & 1] + ph * kPStride + 8 * (kg & 1);
+          *(half4v*)(prow_p + p_col(ph, kg >> 1)) = pf[0];        // rows 4kg..4kg+3
+          *(half4v*)(prow_p + p_col(ph, 2 + (kg >> 1))) = pf[1];  // rows 16+4kg..
           const uint64_t any = __ballot(move && i > 0);
           if (lane == 0) flag_s[i & 1][w] = any != 0ull;
           if (kg == 0) alpha_s[i & 1][16 * w + l16] = alpha;
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         half8v pa[NH];
 #pragma unroll
         for (int hb = 0; hb < NH; ++hb)
-          pa[hb] = *(const half8v*)(pbuf[j & 1] + (16 * hb + l16) * kPStride + 16 * kg);
+          pa[hb] = *(const half8v*)(pbuf[j & 1] + (16 * hb + l16) * kPStride + p_col(16 * hb + l16, kg));
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const int ng = 4 * pw + n;
