@@ -65,7 +65,7 @@ class SparseWorkload:
     """
 
     def __init__(self, name, B, q_len, H, ctx, topk, append_rows, rotations, seed, device,
-                 q_lens=None, keep_latent=False, fmt="nvfp4", overlap=None):
+                 q_lens=None, keep_latent=False, fmt="nvfp4", overlap=None, q_dtype="bf16"):
         import torch
         from nvfp4_compressed_mla_amd import workloads as wl
         import nvfp4_compressed_mla_amd as m
@@ -96,7 +96,8 @@ class SparseWorkload:
         self.new_slots = torch.cat([wl.slot_mapping_for(bt, b, existing[b], append_rows)
                                     for b in range(B)])
         self.rot = rotations
-        self.q = [wl.gen_queries(B, q_len, H, "bf16", seed + 100 + r, device) for r in range(rotations)]
+        self.q_dtype = q_dtype
+        self.q = [wl.gen_queries(B, q_len, H, q_dtype, seed + 100 + r, device) for r in range(rotations)]
         if overlap is not None:
             self.idx = [wl.gen_topk_overlap(B, q_len, topk, self.ctx, overlap, seed + 200 + r, device)
                         for r in range(rotations)]
@@ -138,7 +139,14 @@ class SparseWorkload:
     # algorithmic bytes / flops of the fused decode kernel for rotation r
     def kernel_bytes(self, r):
         T = self.B * self.q_len
-        return self.valid_pairs[r] * (self.row_bytes + 4 + 4) + T * self.H * 576 * 2
+        qb = 4 if self.q_dtype == "fp32" else 2
+        return self.valid_pairs[r] * (self.row_bytes + 4 + 4) + T * self.H * 576 * qb
+
+    def launch_bytes(self, r):
+        """The whole decode launch (fused kernel + combine): the kernel's bytes plus the fp32
+        output and lse it finally writes."""
+        T = self.B * self.q_len
+        return self.kernel_bytes(r) + T * self.H * (512 + 1) * 4
 
     def gathered_bytes(self, r):
         return self.valid_pairs[r] * self.row_bytes
@@ -148,9 +156,8 @@ class SparseWorkload:
 
     def step_bytes(self, r):
         """Whole-step algorithmic bytes: append (bf16 in, 352 B out, slot) + decode incl. output."""
-        T = self.B * self.q_len
         app = self.append_rows * self.B * (1152 + 352 + 8)
-        return app + self.kernel_bytes(r) + T * self.H * (512 + 1) * 4
+        return app + self.launch_bytes(r)
 
 
 class DenseWorkload:
@@ -191,6 +198,9 @@ class DenseWorkload:
     def kernel_bytes(self, r):
         return self.B * self.ctx * (352 + 4 / 64) + self.B * self.H * 576 * 2
 
+    def launch_bytes(self, r):
+        return self.kernel_bytes(r) + self.B * self.H * (512 + 1) * 4
+
     def gathered_bytes(self, r):
         return self.B * self.ctx * 352
 
@@ -218,29 +228,52 @@ def capture(fn, n, offset=0):
     return g
 
 
-def time_steps(fn, rot, steps, warmup):
-    """Replay captured graphs for `warmup` then exactly `steps` steps; returns wall ms per step."""
+def _graph_plan(rot, n, tail_at_end):
+    """Whole graphs covering n steps: (steps, first rotation) per replay. Full rotation graphs
+    first; the remainder n % rot is one graph of that many consecutive steps, over the first
+    rotations (timed region) or the last ones (warmup, so that the timed steps that follow start
+    on rotations the warmup did not just read)."""
+    plan = [(rot, 0)] * (n // rot)
+    r = n % rot
+    if r:
+        plan.append((r, rot - r if tail_at_end else 0))
+    return plan
+
+
+def time_steps(fn, rot, steps, warmup, stats=None):
+    """Replay captured graphs for `warmup` then exactly `steps` steps; returns wall ms per step.
+
+    Every replay is a whole multi-step graph (a full pass over the `rot` rotations, or one graph
+    of the remaining steps), so the per-step figure does not depend on how `steps` divides by
+    `rot`. When `stats` is a dict it receives the per-replay step times (HIP events around each
+    replay on the replay stream): median, p10, p90 (us per step) and the replay count.
+    """
     import torch
-    full = capture(fn, rot)
-    singles = {}
-
-    def run(n):
-        for _ in range(n // rot):
-            full.replay()
-        for r in range(n % rot):
-            if r not in singles:
-                singles[r] = capture(fn, 1, r)
-            singles[r].replay()
-
-    # capture any single-step graphs the timed region needs before timing
-    for r in range(steps % rot):
-        singles[r] = capture(fn, 1, r)
-    run(warmup)
+    graphs = {}
+    warm_plan = _graph_plan(rot, warmup, True)
+    time_plan = _graph_plan(rot, steps, False)
+    for key in set(warm_plan + time_plan):
+        graphs[key] = capture(fn, key[0], key[1])
+    for key in warm_plan:
+        graphs[key].replay()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in time_plan]
     t0 = time.perf_counter()
-    run(steps)
+    for key, (a, b) in zip(time_plan, evs):
+        a.record()
+        graphs[key].replay()
+        b.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if stats is not None:
+        per = sorted(a.elapsed_time(b) * 1e3 / key[0] for key, (a, b) in zip(time_plan, evs))
+
+        def pct(q):
+            return per[min(len(per) - 1, max(0, int(round(q * (len(per) - 1)))))]
+        stats.update({"median_us": round(pct(0.5), 3), "p10_us": round(pct(0.1), 3),
+                      "p90_us": round(pct(0.9), 3), "replays": len(per),
+                      "steps_per_replay": sorted({k[0] for k in time_plan})})
     return (t1 - t0) * 1e3 / steps
 
 
@@ -468,20 +501,26 @@ def cpu_baseline(wk, budget_s=12.0):
 
 def run_config(wk, steps, warmup, prof_launches):
     """Graph-timed decode launches plus event-timed fused kernel for one extra config."""
-    ms = time_steps(wk.decode, wk.rot, steps, warmup)
+    st = {}
+    ms = time_steps(wk.decode, wk.rot, steps, warmup, st)
     kavg, _ = time_decode_kernel(wk, prof_launches)
     nb = sum(wk.kernel_bytes(r) for r in range(wk.rot)) / wk.rot
+    lb = sum(wk.launch_bytes(r) for r in range(wk.rot)) / wk.rot
     gb = sum(wk.gathered_bytes(r) for r in range(wk.rot)) / wk.rot
     fl = sum(wk.flops(r) for r in range(wk.rot)) / wk.rot
     return {
         "us_per_launch": round(ms * 1e3, 2),
+        "launch_replays_us": st,
         "fused_kernel_us": round(kavg * 1e3, 2),
         "gathered_GBps": round(gb / (ms * 1e-3) / 1e9, 1),
         "kernel_GBps": round(nb / (kavg * 1e-3) / 1e9, 1),
         "kernel_hbm_frac": round(nb / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "launch_GBps": round(lb / (ms * 1e-3) / 1e9, 1),
+        "launch_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernel_TFLOPs": round(fl / (kavg * 1e-3) / 1e12, 1),
         "kernel_mfma_frac": round(fl / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
         "splits": wk.splits,
+        **({"q_dtype": wk.q_dtype} if getattr(wk, "q_dtype", "bf16") != "bf16" else {}),
         **({"note": "fused_kernel_us is the FP8 decode kernel alone; us_per_launch includes the "
                     "staging pass and the combine"} if getattr(wk, "fmt", "") == "staged" else {}),
     }
@@ -537,14 +576,16 @@ def main():
                         keep_latent=not args.no_cpu_baseline)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; splits={wk.splits}")
 
-    ms_step = time_steps(wk.step, wk.rot, args.steps, args.warmup)
-    log(f"[bench] step {ms_step * 1e3:.2f} us")
-    ms_dec = time_steps(wk.decode, wk.rot, max(args.steps // 2, wk.rot), args.warmup)
+    step_stats, dec_stats = {}, {}
+    ms_step = time_steps(wk.step, wk.rot, args.steps, args.warmup, step_stats)
+    log(f"[bench] step {ms_step * 1e3:.2f} us (replays: {step_stats})")
+    ms_dec = time_steps(wk.decode, wk.rot, max(args.steps // 2, wk.rot), args.warmup, dec_stats)
     kavg, kd = time_decode_kernel(wk, args.prof_launches)
     log(f"[bench] decode launch {ms_dec * 1e3:.2f} us, fused kernel {kavg * 1e3:.2f} us")
 
     gathered = sum(wk.gathered_bytes(r) for r in range(wk.rot)) / wk.rot
     kbytes = sum(wk.kernel_bytes(r) for r in range(wk.rot)) / wk.rot
+    lbytes = sum(wk.launch_bytes(r) for r in range(wk.rot)) / wk.rot
     flops = sum(wk.flops(r) for r in range(wk.rot)) / wk.rot
     achieved = kbytes / (kavg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
@@ -568,7 +609,9 @@ def main():
                                "block tables",
                    "global_batch": 32, "seq_len": 143360, "topk": 2048, "heads": 64,
                    "rotations": wk.rot, "splits": wk.splits},
+        "step_replays_us": step_stats,
         "us_per_launch": round(ms_dec * 1e3, 2),
+        "launch_replays_us": dec_stats,
         "gathered_GBps_per_launch": round(gathered / (ms_dec * 1e-3) / 1e9, 1),
         "gathered_pct_of_peak": round(100 * gathered / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {
@@ -584,6 +627,20 @@ def main():
             "mfma_TFLOPs": round(flops / (kavg * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
             "kernel_source_sha256_16": src_hash,
+            "timing_note": "kernel_us comes from HIP events the library records around the fused "
+                           "kernel on its launch stream (eager launches); against the rocprofv3 "
+                           "kernel trace they include about 1-3 us of command-packet time",
+        },
+        "roofline_launch": {
+            "bound": "hbm",
+            "what": "whole decode launch (fused kernel + split combine), graph-replayed; bytes "
+                    "include the fp32 output and lse",
+            "achieved": round(lbytes / (ms_dec * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(lbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes_per_launch": int(lbytes),
+            "launch_us": round(ms_dec * 1e3, 3),
         },
         "context": {"pages_GB200_us_per_launch_15tok_16heads": 12.0},
     }
@@ -597,7 +654,7 @@ def main():
         for name, key, mk in (
             ("pages", "pages_shape_T15_H16", lambda: SparseWorkload("pages", 1, 15, 16, [149504], 2048, 0, 64, 1101, dev)),
             ("mtp", "mtp_B16_q15_H64", lambda: SparseWorkload("mtp", 16, 15, 64, [149504] * 16, 2048, 0, 6, 1002, dev)),
-            ("tiny", "tiny_B1_H16_k256", lambda: SparseWorkload("tiny", 1, 1, 16, [4096], 256, 0, 8, 1000, dev)),
+            ("tiny", "tiny_B1_H16_k256_fp32q", lambda: SparseWorkload("tiny", 1, 1, 16, [4096], 256, 0, 8, 1000, dev, q_dtype="fp32")),
         ):
             if name not in wanted:
                 continue

@@ -268,6 +268,36 @@ mla_status mla_set_timing_events(hipEvent_t start, hipEvent_t stop);
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 
+/* ---- Opt-in content checks (MLA_DEBUG_CHECKS) ------------------------------------------------
+ * Index values, page ids, slots and sequence lengths are the caller's contract: the kernels treat
+ * a bad entry as an empty slot (nothing loaded or written) and report nothing. With the checks on
+ * -- mla_set_debug_checks(1), or the environment variable MLA_DEBUG_CHECKS set to anything but
+ * "0" when the library makes its first decision -- every append, decode and staging entry point
+ * first copies its index arrays to the host (synchronizing `stream`; not usable under graph
+ * capture, where the copy fails with MLA_ERR_HIP) and returns MLA_ERR_INVALID_ARG, with the first
+ * offending entry in mla_last_error(), instead of launching when an entry would be skipped:
+ *   - a topk_idx entry below -1, at or past max_pages*64, in an unmapped (negative) page, or whose
+ *     row [page*page_stride + (j%64)*row_bytes, +row_bytes) is not inside [0, cache_bytes);
+ *   - a seq_lens value below 0 or above max_pages*64, or a page among the first ceil(seq_len/64)
+ *     that is unmapped or whose used rows fall outside the cache;
+ *   - a slot_mapping entry below -1 or whose row falls outside the cache.
+ * Off by default: the hot path then neither copies nor synchronizes. */
+mla_status mla_set_debug_checks(int32_t enabled);
+int32_t mla_debug_checks_enabled(void);
+
+/* The same checks on HOST arrays (no HIP call; usable without a GPU). row_bytes is 352 for NVFP4
+ * rows and 576 for FP8 rows. Return MLA_OK or MLA_ERR_INVALID_ARG with mla_last_error() set. */
+mla_status mla_check_sparse_indices(const int32_t* topk_idx, int32_t B, int32_t q_len,
+                                    int32_t topk, const int32_t* block_table, int32_t max_pages,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    int64_t row_bytes);
+mla_status mla_check_dense_tables(const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  int64_t page_stride_bytes, int64_t cache_bytes,
+                                  int64_t row_bytes);
+mla_status mla_check_slots(const int64_t* slots, int64_t n, int64_t page_stride_bytes,
+                           int64_t cache_bytes, int64_t row_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,11 @@ from ._lib import (  # noqa: F401
     MLA_LAYOUT_LAYER_MAJOR,
     MlaError,
     load_library,
+    mla_check_dense_tables,
+    mla_check_slots,
+    mla_check_sparse_indices,
     mla_copy_kv_blocks,
+    mla_debug_checks_enabled,
     mla_decode_workspace_size,
     mla_dense_decode,
     mla_dense_decode_num_splits,
@@ -21,6 +25,7 @@ from ._lib import (  # noqa: F401
     mla_nvfp4_dequantize_rows,
     mla_nvfp4_quantize_append,
     mla_nvfp4_stage_fp8,
+    mla_set_debug_checks,
     mla_set_timing_events,
     mla_sparse_decode,
     mla_sparse_decode_num_splits,

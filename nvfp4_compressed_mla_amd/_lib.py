@@ -44,6 +44,11 @@ EXPORTED = [
     "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
+    "mla_set_debug_checks",
+    "mla_debug_checks_enabled",
+    "mla_check_sparse_indices",
+    "mla_check_dense_tables",
+    "mla_check_slots",
 ]
 
 
@@ -116,6 +121,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_set_debug_checks.argtypes = [i32]
+    lib.mla_set_debug_checks.restype = ctypes.c_int
+    lib.mla_debug_checks_enabled.argtypes = []
+    lib.mla_debug_checks_enabled.restype = i32
+    lib.mla_check_sparse_indices.argtypes = [vp, i32, i32, i32, vp, i32, i64, i64, i64]
+    lib.mla_check_sparse_indices.restype = ctypes.c_int
+    lib.mla_check_dense_tables.argtypes = [vp, i32, i32, vp, i32, i64, i64, i64]
+    lib.mla_check_dense_tables.restype = ctypes.c_int
+    lib.mla_check_slots.argtypes = [vp, i64, i64, i64, i64]
+    lib.mla_check_slots.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -462,3 +477,46 @@ def mla_topk_indices(scores, seq_lens, k: int, out=None, workspace=None, stream=
 def mla_set_timing_events(start, stop) -> None:
     """Record raw HIP events (handles as ints / c_void_p, or None) around the fused decode kernel."""
     _check(load_library().mla_set_timing_events(start, stop))
+
+
+def mla_set_debug_checks(enabled: bool) -> None:
+    """Turn the library's opt-in content checks of index arrays on or off (off by default; the
+    environment variable MLA_DEBUG_CHECKS=1 turns them on at the first call)."""
+    _check(load_library().mla_set_debug_checks(1 if enabled else 0))
+
+
+def mla_debug_checks_enabled() -> bool:
+    return bool(load_library().mla_debug_checks_enabled())
+
+
+def _host_i32(a):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def mla_check_sparse_indices(topk_idx, block_table, page_stride_bytes, cache_bytes,
+                             row_bytes=ROW_BYTES) -> None:
+    """Host check of a sparse call's index list [B, q_len, topk] against its block table
+    [B, max_pages] (host arrays); raises MlaError naming the first bad entry."""
+    idx, bt = _host_i32(topk_idx), _host_i32(block_table)
+    B, q_len, topk = idx.shape
+    _check(load_library().mla_check_sparse_indices(
+        idx.ctypes.data_as(ctypes.c_void_p), B, q_len, topk, bt.ctypes.data_as(ctypes.c_void_p),
+        bt.shape[1], int(page_stride_bytes), int(cache_bytes), int(row_bytes)))
+
+
+def mla_check_dense_tables(seq_lens, q_len, block_table, page_stride_bytes, cache_bytes,
+                           row_bytes=ROW_BYTES) -> None:
+    """Host check of a dense call's seq_lens [B] and block table [B, max_pages]."""
+    sl, bt = _host_i32(seq_lens), _host_i32(block_table)
+    _check(load_library().mla_check_dense_tables(
+        sl.ctypes.data_as(ctypes.c_void_p), sl.size, int(q_len), bt.ctypes.data_as(ctypes.c_void_p),
+        bt.shape[1], int(page_stride_bytes), int(cache_bytes), int(row_bytes)))
+
+
+def mla_check_slots(slots, page_stride_bytes, cache_bytes, row_bytes=ROW_BYTES) -> None:
+    """Host check of an append's slot_mapping (int64 host array)."""
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    _check(load_library().mla_check_slots(sl.ctypes.data_as(ctypes.c_void_p), sl.size,
+                                          int(page_stride_bytes), int(cache_bytes), int(row_bytes)))

@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <vector>
+
 #include "../../include/mla_nvfp4.h"
 #include "mla_internal.h"
 
@@ -47,6 +50,33 @@ mla_status check_cache(const void* kv_cache, int64_t page_stride, int64_t cache_
   if (cache_bytes < row_bytes || cache_bytes > kMaxCacheBytes)
     return fail(MLA_ERR_INVALID_ARG, "cache_bytes %lld out of range [%lld, 2^36]", (long long)cache_bytes,
                 (long long)row_bytes);
+  return MLA_OK;
+}
+
+// ---- opt-in content checks (MLA_DEBUG_CHECKS) ------------------------------------------------
+// -1 = not decided yet (the environment is read at the first call), 0 = off, 1 = on.
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on() {
+  int v = g_debug_checks.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = getenv("MLA_DEBUG_CHECKS");
+    v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug_checks.compare_exchange_strong(expected, v);
+    v = g_debug_checks.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+// Copies n elements of a device array to the host, synchronizing `stream` (debug checks only).
+template <class T>
+mla_status debug_copy(std::vector<T>& v, const T* dev, size_t n, hipStream_t stream, const char* what) {
+  v.resize(n);
+  if (n == 0) return MLA_OK;
+  hipError_t e = hipMemcpyAsync(v.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "debug checks: copy of %s: %s", what, hipGetErrorString(e));
   return MLA_OK;
 }
 
@@ -146,6 +176,87 @@ const char* mla_status_string(mla_status s) {
 
 const char* mla_last_error(void) { return g_last_error; }
 
+mla_status mla_set_debug_checks(int32_t enabled) {
+  g_debug_checks.store(enabled ? 1 : 0, std::memory_order_relaxed);
+  return MLA_OK;
+}
+
+int32_t mla_debug_checks_enabled(void) { return debug_checks_on() ? 1 : 0; }
+
+mla_status mla_check_sparse_indices(const int32_t* topk_idx, int32_t B, int32_t q_len,
+                                    int32_t topk, const int32_t* block_table, int32_t max_pages,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    int64_t row_bytes) {
+  if (!topk_idx || !block_table || B < 1 || q_len < 1 || topk < 1 || max_pages < 1)
+    return fail(MLA_ERR_INVALID_ARG, "check_sparse_indices: null array or empty shape");
+  const int64_t limit = (int64_t)max_pages * MLA_PAGE_ROWS;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t t = 0; t < q_len; ++t)
+      for (int32_t s = 0; s < topk; ++s) {
+        const int64_t e = ((int64_t)b * q_len + t) * topk + s;
+        const int32_t j = topk_idx[e];
+        if (j == -1) continue;
+        if (j < 0)
+          return fail(MLA_ERR_INVALID_ARG, "topk_idx[%d][%d][%d] = %d: negative and not -1", b, t, s, j);
+        if (j >= limit)
+          return fail(MLA_ERR_INVALID_ARG, "topk_idx[%d][%d][%d] = %d: beyond the block table (%lld positions)",
+                      b, t, s, j, (long long)limit);
+        const int32_t pg = block_table[(int64_t)b * max_pages + j / MLA_PAGE_ROWS];
+        if (pg < 0)
+          return fail(MLA_ERR_INVALID_ARG, "topk_idx[%d][%d][%d] = %d: block_table[%d][%d] = %d is unmapped",
+                      b, t, s, j, b, j / MLA_PAGE_ROWS, pg);
+        const int64_t off = (int64_t)pg * page_stride_bytes + (int64_t)(j % MLA_PAGE_ROWS) * row_bytes;
+        if (pg > cache_bytes / page_stride_bytes || off + row_bytes > cache_bytes)
+          return fail(MLA_ERR_INVALID_ARG, "topk_idx[%d][%d][%d] = %d: page %d puts the row at byte %lld, "
+                      "outside the %lld-byte cache", b, t, s, j, pg, (long long)off, (long long)cache_bytes);
+      }
+  return MLA_OK;
+}
+
+mla_status mla_check_dense_tables(const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  int64_t page_stride_bytes, int64_t cache_bytes,
+                                  int64_t row_bytes) {
+  if (!seq_lens || !block_table || B < 1 || q_len < 1 || max_pages < 1)
+    return fail(MLA_ERR_INVALID_ARG, "check_dense_tables: null array or empty shape");
+  const int64_t limit = (int64_t)max_pages * MLA_PAGE_ROWS;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = seq_lens[b];
+    if (n < 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %lld is negative", b, (long long)n);
+    if (n > limit)
+      return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %lld exceeds the block table (%lld positions)",
+                  b, (long long)n, (long long)limit);
+    for (int64_t p = 0; p * MLA_PAGE_ROWS < n; ++p) {
+      const int32_t pg = block_table[(int64_t)b * max_pages + p];
+      if (pg < 0)
+        return fail(MLA_ERR_INVALID_ARG, "block_table[%d][%lld] = %d is unmapped inside seq_lens[%d] = %lld",
+                    b, (long long)p, pg, b, (long long)n);
+      const int64_t rows = n - p * MLA_PAGE_ROWS < MLA_PAGE_ROWS ? n - p * MLA_PAGE_ROWS : MLA_PAGE_ROWS;
+      const int64_t end = (int64_t)pg * page_stride_bytes + rows * row_bytes;
+      if (pg > cache_bytes / page_stride_bytes || end > cache_bytes)
+        return fail(MLA_ERR_INVALID_ARG, "block_table[%d][%lld] = %d: rows end at byte %lld, outside the "
+                    "%lld-byte cache", b, (long long)p, pg, (long long)end, (long long)cache_bytes);
+    }
+  }
+  return MLA_OK;
+}
+
+mla_status mla_check_slots(const int64_t* slots, int64_t n, int64_t page_stride_bytes,
+                           int64_t cache_bytes, int64_t row_bytes) {
+  if (n < 0 || (n > 0 && !slots)) return fail(MLA_ERR_INVALID_ARG, "check_slots: null array or negative n");
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t s = slots[i];
+    if (s == -1) continue;
+    if (s < 0) return fail(MLA_ERR_INVALID_ARG, "slot_mapping[%lld] = %lld: negative and not -1", (long long)i, (long long)s);
+    const int64_t pg = s / MLA_PAGE_ROWS;
+    if (pg > (cache_bytes / page_stride_bytes) + 1 ||
+        pg * page_stride_bytes + (s % MLA_PAGE_ROWS) * row_bytes + row_bytes > cache_bytes)
+      return fail(MLA_ERR_INVALID_ARG, "slot_mapping[%lld] = %lld: the row falls outside the %lld-byte cache",
+                  (long long)i, (long long)s, (long long)cache_bytes);
+  }
+  return MLA_OK;
+}
+
 mla_status mla_set_timing_events(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr))
     return fail(MLA_ERR_INVALID_ARG, "timing events must be both set or both null");
@@ -169,6 +280,11 @@ mla_status mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stri
   if (!aligned(rope, 2) || rope_row_stride < MLA_ROPE_DIM)
     return fail(MLA_ERR_INVALID_ARG, "rope must be 2-byte aligned with a row stride >= 64");
   if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  if (debug_checks_on()) {
+    std::vector<int64_t> hs;
+    if ((st = debug_copy(hs, slot_mapping, (size_t)n_rows, stream, "slot_mapping")) != MLA_OK) return st;
+    if ((st = mla_check_slots(hs.data(), n_rows, page_stride_bytes, cache_bytes, MLA_ROW_BYTES)) != MLA_OK) return st;
+  }
   return hip_status(mla::launch_quantize_append(latent, latent_row_stride, rope, rope_row_stride,
                                                 slot_mapping, n_rows, kv_cache, page_stride_bytes,
                                                 cache_bytes, stream),
@@ -257,6 +373,14 @@ mla_status sparse_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const 
     a.ws_o = (_Float16*)workspace;
     a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
   }
+  if (debug_checks_on()) {
+    std::vector<int32_t> hi, hb;
+    if ((st = debug_copy(hi, topk_idx, (size_t)(T * topk), stream, "topk_idx")) != MLA_OK) return st;
+    if ((st = debug_copy(hb, block_table, (size_t)B * max_pages, stream, "block_table")) != MLA_OK) return st;
+    st = mla_check_sparse_indices(hi.data(), B, q_len, topk, hb.data(), max_pages, page_stride_bytes,
+                                  cache_bytes, fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
+    if (st != MLA_OK) return st;
+  }
   return run_decode(a, H, false, fp8, stream);
 }
 
@@ -299,6 +423,14 @@ mla_status dense_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const v
   if (num_splits > 1) {
     a.ws_o = (_Float16*)workspace;
     a.ws_lse = (float*)(a.ws_o + T * num_splits * H * MLA_LATENT_DIM);
+  }
+  if (debug_checks_on()) {
+    std::vector<int32_t> hs, hb;
+    if ((st = debug_copy(hs, seq_lens, (size_t)B, stream, "seq_lens")) != MLA_OK) return st;
+    if ((st = debug_copy(hb, block_table, (size_t)B * max_pages, stream, "block_table")) != MLA_OK) return st;
+    st = mla_check_dense_tables(hs.data(), B, q_len, hb.data(), max_pages, page_stride_bytes,
+                                cache_bytes, fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
+    if (st != MLA_OK) return st;
   }
   return run_decode(a, H, true, fp8, stream);
 }
@@ -386,6 +518,11 @@ mla_status mla_fp8_append(const void* latent, int64_t latent_row_stride, const v
   if (!aligned(rope, 2) || rope_row_stride < MLA_ROPE_DIM)
     return fail(MLA_ERR_INVALID_ARG, "rope must be 2-byte aligned with a row stride >= 64");
   if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  if (debug_checks_on()) {
+    std::vector<int64_t> hs;
+    if ((st = debug_copy(hs, slot_mapping, (size_t)n_rows, stream, "slot_mapping")) != MLA_OK) return st;
+    if ((st = mla_check_slots(hs.data(), n_rows, page_stride_bytes, cache_bytes, MLA_FP8_ROW_BYTES)) != MLA_OK) return st;
+  }
   return hip_status(mla::launch_fp8_append(latent, latent_row_stride, rope, rope_row_stride,
                                            slot_mapping, n_rows, kv_cache, page_stride_bytes,
                                            cache_bytes, stream),
@@ -410,6 +547,14 @@ mla_status mla_nvfp4_stage_fp8(const void* kv_cache, int64_t page_stride_bytes, 
     return fail(MLA_ERR_INVALID_ARG, "misaligned staged buffers or index arrays");
   const int64_t T = (int64_t)B * q_len;
   if (T > (int64_t)1 << 20) return fail(MLA_ERR_INVALID_ARG, "too many query tokens");
+  if (debug_checks_on()) {
+    std::vector<int32_t> hi, hb;
+    if ((st = debug_copy(hi, topk_idx, (size_t)(T * topk), stream, "topk_idx")) != MLA_OK) return st;
+    if ((st = debug_copy(hb, block_table, (size_t)B * max_pages, stream, "block_table")) != MLA_OK) return st;
+    st = mla_check_sparse_indices(hi.data(), B, q_len, topk, hb.data(), max_pages, page_stride_bytes,
+                                  cache_bytes, MLA_ROW_BYTES);
+    if (st != MLA_OK) return st;
+  }
   return hip_status(mla::launch_stage_fp8(kv_cache, page_stride_bytes, cache_bytes, block_table,
                                           max_pages, topk_idx, topk, (int32_t)T, q_len, staged_rows,
                                           staged_idx, staged_block_table, stream),

@@ -4,9 +4,11 @@
 // section "Making room for low-latency decode": the MLA latent is compressed to NVFP4 -- 4-bit
 // values with one FP8 scale per 16 values -- and the 64-value rope part stays FP8) is a pure
 // streaming pass: 1152 bytes of bf16 in, one 352-byte row out, so it is bound by HBM bandwidth.
-// Each lane encodes one 16-value group with exact integer/compare arithmetic (scale byte, then
-// sixteen 4-bit codes) and two rope values; a row leaves as two stores: 256 code bytes (8 per
-// lane), then 8 scale dwords and 16 rope dwords gathered with lane shuffles.
+// Each lane encodes one 16-value group and two rope values: the scale byte is the gfx950 E4M3
+// conversion of amax * fl32(1/6), the sixteen 4-bit codes are the gfx950 E2M1 conversion of an
+// fma-corrected quotient x / scale (exact on every E2M1 grid midpoint, so the conversion's ties
+// to even give the format's rounding); a row leaves as two stores: 256 code bytes (8 per lane),
+// then 8 scale dwords and 16 rope dwords gathered with lane shuffles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

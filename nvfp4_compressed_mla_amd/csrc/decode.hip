@@ -287,9 +287,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     n_rows = max(0, min(vis, p0 + a.split_rows) - p0);
     const int n_pages = (n_rows + 63) >> 6;
     for (int i = tid; i < n_pages; i += kThreads) {
+      // The page's byte offset is checked in 64 bits before it is narrowed to 16-byte units:
+      // a page starting at or past cache_bytes (<= 2^36) is marked invalid, so a page id whose
+      // offset exceeds 2^36 can never wrap onto a real page.
       const int pg = bt[(p0 >> 6) + i];
       const int64_t off = (int64_t)pg * a.page_stride;
-      rowoff[i] = (pg < 0) ? kInvalid : (uint32_t)(off >> 4);
+      rowoff[i] = (pg < 0 || off >= a.cache_bytes) ? kInvalid : (uint32_t)(off >> 4);
     }
     lds_barrier();                                         // same barrier count as the sparse path
   }
@@ -367,8 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     } else {
       const int pos = p0 + (ok ? row : 0);
       const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-      const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
-      return (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
+      const int64_t o = (int64_t)pb + (pos & 63) * (RB / 16);     // 64-bit: no wrap
+      return (ok && pb != kInvalid && o * 16 + RB <= a.cache_bytes) ? (uint32_t)o : kInvalid;
     }
   };
   auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
@@ -540,8 +543,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         const bool ok = row < n_rows;
         const int pos = p0 + (ok ? row : 0);
         const uint32_t pb = rowoff[(pos >> 6) - (p0 >> 6)];
-        const uint32_t o = pb + (uint32_t)(pos & 63) * (RB / 16);
-        o16 = (ok && pb != kInvalid && (int64_t)o * 16 + RB <= a.cache_bytes) ? o : kInvalid;
+        const int64_t o = (int64_t)pb + (pos & 63) * (RB / 16);   // 64-bit: no wrap
+        o16 = (ok && pb != kInvalid && o * 16 + RB <= a.cache_bytes) ? (uint32_t)o : kInvalid;
       }
       return o16 != kInvalid ? a.cache + (int64_t)o16 * 16 : g_zero_row;
     };

@@ -101,19 +101,20 @@ def pages_for(ctx: int) -> int:
 def gen_block_table(ctx: list, seed: int, device="cpu", spare_pages: int = 0):
     """Random page assignment: a permutation of all physical pages, sliced per request.
 
-    Returns (block_table int32 [B, max_pages] padded with 0, total physical pages).
+    Returns (block_table int32 [B, max_pages] padded with 0, total physical pages). The table is
+    built on the host and moved to ``device`` with one copy.
     """
-    g = _gen(seed, device)
+    g = _gen(seed, "cpu")
     need = [pages_for(c) for c in ctx]
     total = sum(need) + spare_pages
-    perm = torch.randperm(total, generator=g, device=device).to(torch.int32)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
     max_pages = max(need) if need else 1
-    bt = torch.zeros(len(ctx), max_pages, dtype=torch.int32, device=device)
+    bt = torch.zeros(len(ctx), max_pages, dtype=torch.int32)
     o = 0
     for b, n in enumerate(need):
         bt[b, :n] = perm[o:o + n]
         o += n
-    return bt, total
+    return bt.to(device), total
 
 
 def slot_mapping_for(block_table, b: int, start: int, count: int):
@@ -127,23 +128,24 @@ def gen_topk(B: int, q_len: int, k: int, ctx: list, seed: int, device="cpu", q_l
     """Top-k lists int32 [B, q_len, k]: k distinct uniform positions in [0, ctx_b) per token.
 
     Contexts shorter than k list every position once, padded with -1 at random list places.
-    Rows of requests with fewer query tokens than q_len (mixed steps) are all -1.
+    Rows of requests with fewer query tokens than q_len (mixed steps) are all -1. The lists are
+    drawn on the host and moved to ``device`` with one copy.
     """
-    g = _gen(seed, device)
-    out = torch.full((B, q_len, k), -1, dtype=torch.int32, device=device)
+    g = _gen(seed, "cpu")
+    out = torch.full((B, q_len, k), -1, dtype=torch.int32)
     for b in range(B):
         n_q = q_lens[b] if q_lens else q_len
         c = int(ctx[b])
         for t in range(n_q):
+            keys = torch.rand(c, generator=g)
             if c >= k:
-                keys = torch.rand(c, generator=g, device=device)
-                out[b, t] = torch.argsort(keys)[:k].to(torch.int32)
+                # the k smallest keys in ascending key order (the first k of their argsort)
+                out[b, t] = torch.topk(keys, k, largest=False, sorted=True).indices.to(torch.int32)
             else:
-                keys = torch.rand(c, generator=g, device=device)
                 sel = torch.argsort(keys).to(torch.int32)
-                place = torch.argsort(torch.rand(k, generator=g, device=device))[:c]
+                place = torch.argsort(torch.rand(k, generator=g))[:c]
                 out[b, t, place] = sel
-    return out
+    return out.to(device)
 
 
 def gen_topk_overlap(B: int, q_len: int, k: int, ctx: list, overlap: float, seed: int, device="cpu"):
@@ -153,21 +155,22 @@ def gen_topk_overlap(B: int, q_len: int, k: int, ctx: list, overlap: float, seed
     Per request: a base set of k distinct uniform positions in [0, ctx_b). Each token keeps a
     uniform subset of round(overlap * k) base positions and adds k - that many distinct positions
     from outside the base set. Lists are in ascending position order. Requires ctx_b >= 2k.
+    Drawn on the host and moved to ``device`` with one copy.
     """
-    g = _gen(seed, device)
+    g = _gen(seed, "cpu")
     keep = int(round(overlap * k))
-    out = torch.empty((B, q_len, k), dtype=torch.int32, device=device)
+    out = torch.empty((B, q_len, k), dtype=torch.int32)
     for b in range(B):
         c = int(ctx[b])
         if c < 2 * k:
             raise ValueError("gen_topk_overlap needs ctx >= 2k")
-        perm = torch.randperm(c, generator=g, device=device)
+        perm = torch.randperm(c, generator=g)
         base, rest = perm[:k], perm[k:]
         for t in range(q_len):
-            sub = base[torch.randperm(k, generator=g, device=device)[:keep]]
-            fresh = rest[torch.randperm(c - k, generator=g, device=device)[:k - keep]]
+            sub = base[torch.randperm(k, generator=g)[:keep]]
+            fresh = rest[torch.randperm(c - k, generator=g)[:k - keep]]
             out[b, t] = torch.sort(torch.cat([sub, fresh])).values.to(torch.int32)
-    return out
+    return out.to(device)
 
 
 def gen_topk_batched(B: int, q_len: int, k: int, ctx: int, seed: int, device="cpu"):

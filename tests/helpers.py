@@ -155,7 +155,13 @@ def oracle_staged_cache(case: Case, cache=None) -> np.ndarray:
 
 
 def assert_parity(out, lse, ref_out, ref_lse, tokens=None, what=""):
-    """Row-wise relative error <= ROW_TOL and |lse - ref| <= LSE_TOL on the given tokens."""
+    """Row-wise relative error <= ROW_TOL and |lse - ref| <= LSE_TOL on the given tokens.
+
+    Every compared value must be finite where the reference is: a NaN or infinite output row, or
+    a NaN / wrongly infinite lse, fails (the errors are checked with ``np.isfinite`` before they
+    are folded, so a NaN can never be dropped by the fold). A token whose reference lse is -inf
+    (an empty list) must have exactly zero outputs and lse -inf.
+    """
     out = out.detach().cpu().numpy().astype(np.float64)
     lse = lse.detach().cpu().numpy().astype(np.float64)
     if tokens is None:
@@ -164,11 +170,19 @@ def assert_parity(out, lse, ref_out, ref_lse, tokens=None, what=""):
     worst_lse = 0.0
     for b, t in tokens:
         err = oa.row_relative_error(out[b, t], ref_out[b, t])
+        if not np.all(np.isfinite(err)):
+            bad = np.flatnonzero(~np.isfinite(err))
+            raise AssertionError(f"{what}: token ({b}, {t}) heads {bad[:8].tolist()} have "
+                                 f"non-finite outputs or errors")
         worst = max(worst, float(np.max(err)))
         rl, gl = ref_lse[b, t], lse[b, t]
         both_inf = np.isneginf(rl) & np.isneginf(gl)
         with np.errstate(invalid="ignore"):
             d = np.where(both_inf, 0.0, np.abs(gl - rl))
+        if not np.all(np.isfinite(d)):
+            bad = np.flatnonzero(~np.isfinite(d))
+            raise AssertionError(f"{what}: token ({b}, {t}) heads {bad[:8].tolist()} have lse "
+                                 f"{gl[bad[:4]].tolist()} against {rl[bad[:4]].tolist()}")
         worst_lse = max(worst_lse, float(np.max(d)))
         if np.any(np.isneginf(rl)):
             assert np.all(out[b, t][np.isneginf(rl)] == 0), f"{what}: empty rows must be zero"

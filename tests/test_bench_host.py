@@ -39,3 +39,17 @@ def test_committed_counters_parse_and_exceed_the_algorithmic_bytes():
     assert len(kv["kernel_source_sha256_16"]) == 16
     assert float(kv["hbm_bytes_per_launch"]) >= 65536 * 360 + 32 * 64 * 576 * 2
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_timed_steps_are_whole_graphs_whatever_the_step_count():
+    """Every timed replay is one multi-step graph: full passes over the rotations, then one graph
+    of the remaining steps over the first rotations; the warmup's remainder covers the last
+    rotations, so the timed steps do not start on inputs the warmup just read."""
+    assert bench._graph_plan(48, 20, False) == [(20, 0)]
+    assert bench._graph_plan(48, 960, False) == [(48, 0)] * 20
+    assert bench._graph_plan(48, 100, False) == [(48, 0), (48, 0), (4, 0)]
+    assert bench._graph_plan(48, 5, True) == [(5, 43)]
+    assert bench._graph_plan(48, 96, True) == [(48, 0)] * 2
+    assert bench._graph_plan(48, 0, True) == []
+    for n in (1, 20, 47, 48, 49, 960, 1000):
+        assert sum(k for k, _ in bench._graph_plan(48, n, False)) == n

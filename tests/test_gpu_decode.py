@@ -331,3 +331,99 @@ def test_block_table_width_staged_and_memory_lookups(fmt):
         th.assert_parity(out, lse, ref_o, ref_l, what=f"{fmt} width={width} splits={s}")
         base = next(r for r in results if r[1] == s)
         assert torch.equal(out, base[2]) and torch.equal(lse, base[3]), f"width={width} splits={s}"
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_page_offset_past_2_36_is_an_empty_page(fmt):
+    """A block-table entry whose byte offset (page id x page stride) exceeds 2^36 must be treated
+    as an unmapped page, never as the page its offset would wrap onto in 32-bit 16-byte units.
+    With a 65,536-byte page stride, page id 2^20 + 6 lies at 2^36 + 6 * 65,536: a 32-bit wrap of
+    that offset lands exactly on page 6, which holds real rows of the other request. Dense and
+    sparse decode must both leave the 64 positions of that page out."""
+    from oracle import attention as oa
+    from oracle import cache as oc
+    from oracle import fp8 as f8
+    from oracle import nvfp4 as nv
+    print(f"case: page offset past 2^36 fmt={fmt}", flush=True)
+    m = _m()
+    dev = "cuda"
+    stride = 65536
+    row_bytes = 576 if fmt == "fp8" else 352
+    ctx = [300, 200]
+    B, q_len, H = 2, 1, 64
+    bt_real = torch.tensor([[0, 1, 2, 3, 4], [5, 6, 7, 8, -1]], dtype=torch.int32)
+    cache = torch.zeros(9 * stride, dtype=torch.uint8, device=dev)
+    lat, rope = wl.gen_latent_rope(sum(ctx), 71, dev)
+    slots = torch.cat([wl.slot_mapping_for(bt_real, b, 0, c) for b, c in enumerate(ctx)]).to(dev)
+    (m.mla_fp8_append if fmt == "fp8" else m.mla_nvfp4_quantize_append)(lat, rope, slots, cache, stride)
+    bad = (1 << 20) + 6
+    assert bad * stride >= (1 << 36) and (bad * stride) % (1 << 36) == 6 * stride
+    bt = bt_real.clone()
+    bt[0, 2] = bad                                   # positions 128..191 of request 0
+    bt_d = bt.to(dev)
+    q = wl.gen_queries(B, q_len, H, "bf16", 72, dev)
+    seq = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    scale = th.softmax_scale()
+    dense = m.mla_fp8_dense_decode if fmt == "fp8" else m.mla_dense_decode
+    sparse = m.mla_fp8_sparse_decode if fmt == "fp8" else m.mla_sparse_decode
+    results = [("dense", st, dense(q, cache, stride, bt_d, seq, scale, split_tokens=st)) for st in (64, 4096)]
+    idx = torch.full((B, q_len, 256), -1, dtype=torch.int32)
+    idx[0, 0, :200] = torch.arange(50, 250, dtype=torch.int32)      # crosses the bad page
+    idx[1, 0, :150] = torch.arange(0, 150, dtype=torch.int32)
+    results += [("sparse", s, sparse(q, cache, stride, bt_d, idx.to(dev), scale, num_splits=s)) for s in (1, 2)]
+    torch.cuda.synchronize()
+    # oracle: its own rows at the real slots; the bad page's positions are left out
+    host = np.zeros(9 * stride, dtype=np.uint8)
+    enc = (f8.quantize_rows_fp8 if fmt == "fp8" else nv.quantize_rows)(
+        lat.double().cpu().numpy(), rope.double().cpu().numpy())
+    oc.write_rows(host, stride, slots.cpu().numpy(), enc)
+    keep0 = [j for j in range(300) if not 128 <= j < 192]
+    dense_idx = np.full((B, q_len, 300), -1)
+    dense_idx[0, 0, :len(keep0)] = keep0
+    dense_idx[1, 0, :200] = np.arange(200)
+    q64 = q.float().cpu().numpy().astype(np.float64)
+    ref_d = oa.sparse_decode(q64, host, stride, bt_real.numpy(), dense_idx, scale, row_bytes=row_bytes)
+    sp_idx = idx.numpy().copy()
+    sp_idx[(sp_idx >= 128) & (sp_idx < 192) & (np.arange(B)[:, None, None] == 0)] = -1
+    ref_s = oa.sparse_decode(q64, host, stride, bt_real.numpy(), sp_idx, scale, row_bytes=row_bytes)
+    for kind, arg, (out, lse) in results:
+        ref_o, ref_l = ref_d if kind == "dense" else ref_s
+        th.assert_parity(out, lse, ref_o, ref_l, what=f"{fmt} {kind} {arg} page past 2^36")
+
+
+def test_debug_checks_reject_bad_entries_on_device_calls():
+    """With the opt-in checks on, a device call whose list holds an entry the kernel would skip
+    (an unmapped page) fails with MLA_ERR_INVALID_ARG before launching; with them off the same call
+    runs and treats the entry as empty (parity with the list that has -1 there)."""
+    print("case: debug checks on device calls", flush=True)
+    m = _m()
+    case = th.build_case(2, 1, 16, [900, 500], 256, seed=77)
+    bt = case.block_table.clone()
+    bt[1, 7] = -1                                   # positions 448..499 of request 1 unmapped
+    idx = case.topk_idx.clone()
+    idx[1, 0, 3] = 460
+    before = m.mla_debug_checks_enabled()
+    try:
+        m.mla_set_debug_checks(True)
+        with pytest.raises(m.MlaError, match="unmapped"):
+            m.mla_sparse_decode(case.q, case.cache, case.page_stride, bt, idx, th.softmax_scale())
+        with pytest.raises(m.MlaError, match="unmapped"):
+            m.mla_dense_decode(case.q, case.cache, case.page_stride, bt, case.seq_lens, th.softmax_scale())
+        bad_slots = torch.tensor([0, -3], dtype=torch.int64, device="cuda")
+        with pytest.raises(m.MlaError, match="negative"):
+            m.mla_nvfp4_quantize_append(case.latent[:2], case.rope[:2], bad_slots, case.cache,
+                                        case.page_stride)
+        out, lse = m.mla_sparse_decode(case.q, case.cache, case.page_stride, case.block_table,
+                                       case.topk_idx, th.softmax_scale())   # a good call passes
+        m.mla_set_debug_checks(False)
+        out_b, lse_b = m.mla_sparse_decode(case.q, case.cache, case.page_stride, bt, idx,
+                                           th.softmax_scale())
+        torch.cuda.synchronize()
+    finally:
+        m.mla_set_debug_checks(before)
+    ref_o, ref_l = th.oracle_sparse(case)
+    th.assert_parity(out, lse, ref_o, ref_l, what="debug checks on, good call")
+    case.topk_idx = idx.clone()
+    case.topk_idx[1, 0, 3] = -1
+    ref_o, ref_l = th.oracle_sparse(case)
+    th.assert_parity(out_b, lse_b, ref_o, ref_l, what="debug checks off, unmapped page skipped")

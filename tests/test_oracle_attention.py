@@ -194,3 +194,28 @@ def test_duplicates_count_twice():
     lat, _ = nv.dequantize_rows(rows[[3, 9]])
     assert np.allclose(out[0, 0, 0], (2 * lat[0] + lat[1]) / 3, rtol=0, atol=1e-12)
     assert abs(lse[0, 0, 0] - math.log(3)) < 1e-14
+
+
+def test_row_relative_error_hand_worked_rows():
+    """The parity comparator on rows worked out by hand: max |out - ref| over the row divided by
+    max |ref| over the row (the absolute error where the reference row is all zero); the result
+    has one value per row of the leading axes, and a NaN anywhere in a row makes that row NaN."""
+    out = np.array([[1.0, 2.0, 3.0],        # worst difference 1 at the last dim, max |ref| 4
+                    [0.5, -1.0, 0.0],       # reference row all zero: absolute error 1
+                    [1000.0, 3.0, 1.0],     # one large entry sets the denominator: 2 / 1000
+                    [-1.0, 0.0, 0.0],       # sign flip: |-1 - 1| / 1
+                    [np.nan, 1.0, 1.0],     # NaN propagates
+                    [np.inf, 1.0, 1.0]])    # an infinite output gives an infinite error
+    ref = np.array([[1.0, 2.0, 4.0],
+                    [0.0, 0.0, 0.0],
+                    [1000.0, 1.0, 1.0],
+                    [1.0, 0.0, 0.0],
+                    [1.0, 1.0, 1.0],
+                    [1.0, 1.0, 1.0]])
+    err = oa.row_relative_error(out, ref)
+    assert err.shape == (6,)
+    assert err[0] == 0.25 and err[1] == 1.0 and err[2] == 0.002 and err[3] == 2.0
+    assert np.isnan(err[4]) and np.isposinf(err[5])
+    # leading axes are kept: [2, 3, dims] -> [2, 3]
+    e3 = oa.row_relative_error(np.zeros((2, 3, 5)), np.ones((2, 3, 5)))
+    assert e3.shape == (2, 3) and np.all(e3 == 1.0)
