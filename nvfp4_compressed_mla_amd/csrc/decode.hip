@@ -223,6 +223,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // ---- rows of this split (producer waves) --------------------------------------------------
   int n_rows = 0;
   int p0 = 0;
+  // Dense: every page of the split is mapped and lies wholly inside the cache, so no row needs a
+  // validity mask beyond the split's row count (rows of other pages are empty slots: left out of
+  // the softmax, as the sparse path's compaction leaves out its invalid entries).
+  bool dense_ok = true;
   if constexpr (!DENSE) {
     // Compact the valid entries of [e0, e0 + cnt) into rowoff (16-byte units), in list order:
     // 4 rounds of 512 entries (all index loads first, then all block-table loads), ballot +
@@ -286,6 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     p0 = split * a.split_rows;
     n_rows = max(0, min(vis, p0 + a.split_rows) - p0);
     const int n_pages = (n_rows + 63) >> 6;
+    int bad = 0;
     for (int i = tid; i < n_pages; i += kThreads) {
       // The page's byte offset is checked in 64 bits before it is narrowed to 16-byte units:
       // a page starting at or past cache_bytes (<= 2^36) is marked invalid, so a page id whose
@@ -293,8 +298,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int pg = bt[(p0 >> 6) + i];
       const int64_t off = (int64_t)pg * a.page_stride;
       rowoff[i] = (pg < 0 || off >= a.cache_bytes) ? kInvalid : (uint32_t)(off >> 4);
+      if (pg < 0 || off + (int64_t)kPageRows * RB > a.cache_bytes) bad = 1;
     }
-    lds_barrier();                                         // same barrier count as the sparse path
+    // one barrier, as on the sparse path; no gather is in flight yet
+    dense_ok = __syncthreads_or(bad) == 0;
   }
   if (tid < 8) flag_s[tid >> 2][tid & 3] = 0;
   if constexpr (!DENSE) {
@@ -440,7 +447,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
           float sv[8];
           float mx = -INFINITY;
-          if ((i + 1) * kTileRows <= n_rows) {               // full tile: no row mask
+          const bool full = (i + 1) * kTileRows <= n_rows && dense_ok;
+          if (full) {                                        // full tile: no row mask
   #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               const float4v sc = acc[rb][0] + acc[rb][1];
@@ -457,7 +465,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int row = i * kTileRows + 16 * rb + 4 * kg + e;
-                sv[4 * rb + e] = (row < n_rows) ? sc[e] * a.scale_log2 : -INFINITY;
+                bool ok = row < n_rows;
+                if constexpr (DENSE) ok = ok && (dense_ok || row_o16(row) != kInvalid);
+                sv[4 * rb + e] = ok ? sc[e] * a.scale_log2 : -INFINITY;
                 mx = fmaxf(mx, sv[4 * rb + e]);
               }
             }
@@ -470,11 +480,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
           half4v pf[2];
           float psum = 0.0f;
+          if (full) {
   #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
-            pf[e >> 2][e & 3] = pv;
-            psum += (float)pv;
+            for (int e = 0; e < 8; ++e) {
+              const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+              pf[e >> 2][e & 3] = pv;
+              psum += (float)pv;
+            }
+          } else {
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              // a masked row is 0 (also while no valid row has been seen: m_new = -inf)
+              const _Float16 pv = (sv[e] == -INFINITY) ? (_Float16)0.0f
+                                                       : (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+              pf[e >> 2][e & 3] = pv;
+              psum += (float)pv;
+            }
           }
           l_run = l_run * alpha + psum;
           m_run = m_new;

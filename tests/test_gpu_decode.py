@@ -339,7 +339,8 @@ def test_page_offset_past_2_36_is_an_empty_page(fmt):
     as an unmapped page, never as the page its offset would wrap onto in 32-bit 16-byte units.
     With a 65,536-byte page stride, page id 2^20 + 6 lies at 2^36 + 6 * 65,536: a 32-bit wrap of
     that offset lands exactly on page 6, which holds real rows of the other request. Dense and
-    sparse decode must both leave the 64 positions of that page out."""
+    sparse decode must both leave the 64 positions of that page out, as they leave out the
+    positions of an unmapped (-1) page inside the context."""
     from oracle import attention as oa
     from oracle import cache as oc
     from oracle import fp8 as f8
@@ -360,6 +361,7 @@ def test_page_offset_past_2_36_is_an_empty_page(fmt):
     assert bad * stride >= (1 << 36) and (bad * stride) % (1 << 36) == 6 * stride
     bt = bt_real.clone()
     bt[0, 2] = bad                                   # positions 128..191 of request 0
+    bt[1, 1] = -1                                    # and an unmapped page: 64..127 of request 1
     bt_d = bt.to(dev)
     q = wl.gen_queries(B, q_len, H, "bf16", 72, dev)
     seq = torch.tensor(ctx, dtype=torch.int32, device=dev)
@@ -378,13 +380,15 @@ def test_page_offset_past_2_36_is_an_empty_page(fmt):
         lat.double().cpu().numpy(), rope.double().cpu().numpy())
     oc.write_rows(host, stride, slots.cpu().numpy(), enc)
     keep0 = [j for j in range(300) if not 128 <= j < 192]
+    keep1 = [j for j in range(200) if not 64 <= j < 128]
     dense_idx = np.full((B, q_len, 300), -1)
     dense_idx[0, 0, :len(keep0)] = keep0
-    dense_idx[1, 0, :200] = np.arange(200)
+    dense_idx[1, 0, :len(keep1)] = keep1
     q64 = q.float().cpu().numpy().astype(np.float64)
     ref_d = oa.sparse_decode(q64, host, stride, bt_real.numpy(), dense_idx, scale, row_bytes=row_bytes)
     sp_idx = idx.numpy().copy()
     sp_idx[(sp_idx >= 128) & (sp_idx < 192) & (np.arange(B)[:, None, None] == 0)] = -1
+    sp_idx[(sp_idx >= 64) & (sp_idx < 128) & (np.arange(B)[:, None, None] == 1)] = -1
     ref_s = oa.sparse_decode(q64, host, stride, bt_real.numpy(), sp_idx, scale, row_bytes=row_bytes)
     for kind, arg, (out, lse) in results:
         ref_o, ref_l = ref_d if kind == "dense" else ref_s
@@ -423,7 +427,9 @@ def test_debug_checks_reject_bad_entries_on_device_calls():
         m.mla_set_debug_checks(before)
     ref_o, ref_l = th.oracle_sparse(case)
     th.assert_parity(out, lse, ref_o, ref_l, what="debug checks on, good call")
-    case.topk_idx = idx.clone()
-    case.topk_idx[1, 0, 3] = -1
+    ref_idx = idx.clone()
+    in_page7 = (ref_idx[1] >= 448) & (ref_idx[1] < 512)      # every entry of request 1 in page 7
+    ref_idx[1][in_page7] = -1
+    case.topk_idx = ref_idx
     ref_o, ref_l = th.oracle_sparse(case)
     th.assert_parity(out_b, lse_b, ref_o, ref_l, what="debug checks off, unmapped page skipped")

@@ -3,9 +3,10 @@
 Each case builds the whole cache on the GPU at its real size (140K-200K-token requests, 64-row
 pages, random block tables), runs the decode with the library's own split choice (the one
 bench.py uses), and compares query tokens -- all heads and all 512 output dims of each -- with
-the fp64 oracle: every token of the batched configuration, two whole requests plus three tokens
-of the MTP one, sampled tokens of the dense and mixed ones. The oracle quantizes, by itself,
-only the bf16 rows those tokens read.
+the fp64 oracle: every output row of the batched, MTP and dense configurations, and sampled
+tokens of the mixed one. The oracle quantizes, by itself, only the bf16 rows those tokens read.
+The MTP and dense comparisons are split over several tests (a module-level fixture runs the GPU
+side once) so that each keeps the oracle's CPU time to about a minute.
 """
 
 import numpy as np
@@ -52,30 +53,65 @@ def test_batched_140k_topk2048():
     _sampled_sparse(case, [(b, 0) for b in range(32)], "batched (every output row)")
 
 
-def test_mtp_146k_q15():
-    """B=16, q_len=15, H=64, 149,504-token caches, independent top-k 2048 per query token."""
+@pytest.fixture(scope="module")
+def mtp_run():
+    """B=16, q_len=15, H=64, 149,504-token caches (6144 rows of each appended by one call),
+    independent top-k 2048 per query token; decoded once with the library's split choice."""
     print("case: mtp B=16 q_len=15 H=64 ctx=149504 k=2048", flush=True)
     case = th.build_case(16, 15, 64, [149504] * 16, 2048, seed=1002, spare_pages=0,
                          topk_fn=lambda B, q, k, ctx, s, d: wl.gen_topk_batched(B, q, k, ctx[0], s, d),
                          append_rows=6144)
-    tokens = [(b, t) for b in (0, 15) for t in range(15)] + [(5, 7), (9, 3), (12, 11)]
-    _sampled_sparse(case, tokens, "mtp (requests 0 and 15 whole, three more tokens)")
+    m = _m()
+    out, lse = m.mla_sparse_decode(case.q, case.cache, case.page_stride, case.block_table,
+                                   case.topk_idx, th.softmax_scale())
+    torch.cuda.synchronize()
+    return case, out, lse
 
 
-def test_dense_146k_split4096():
-    """B=8, q_len=1, H=64, 149,504-token caches, dense over every row, 4096-row splits."""
-    print("case: dense B=8 H=64 ctx=149504 split 4096", flush=True)
+@pytest.mark.parametrize("part", [0, 1])
+def test_mtp_146k_q15_every_row(mtp_run, part):
+    """Every output row of the MTP configuration: requests 8*part .. 8*part+7, all 15 tokens."""
+    case, out, lse = mtp_run
+    idx = case.topk_idx.cpu().numpy()
+    worst = (0.0, 0.0)
+    for b in range(8 * part, 8 * part + 8):
+        tokens = [(b, t) for t in range(15)]
+        cache = th.oracle_cache(case, {b: set(int(j) for j in idx[b].ravel() if j >= 0)})
+        ref_o, ref_l = th.oracle_sparse(case, tokens=tokens, cache=cache)
+        w = th.assert_parity(out, lse, ref_o, ref_l, tokens=tokens, what=f"mtp request {b}")
+        worst = (max(worst[0], w[0]), max(worst[1], w[1]))
+        print(f"mtp request {b}: worst row err {w[0]:.2e} lse {w[1]:.2e}", flush=True)
+    print(f"mtp part {part}: worst row err {worst[0]:.2e} lse {worst[1]:.2e}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dense_run():
+    """B=8, q_len=1, H=64, 149,504-token caches, dense over every row: decoded with the
+    configured 4096-position splits and with the library's one-wave split size."""
+    print("case: dense B=8 H=64 ctx=149504", flush=True)
     case = th.build_case(8, 1, 64, [149504] * 8, 0, seed=1003, spare_pages=0)
     m = _m()
     assert m.mla_dense_decode_num_splits(case.block_table.shape[1], 4096) == 37
-    out, lse = m.mla_dense_decode(case.q, case.cache, case.page_stride, case.block_table,
-                                  case.seq_lens, th.softmax_scale(), split_tokens=4096)
+    runs = {}
+    for st in (4096, 0):
+        runs[st] = m.mla_dense_decode(case.q, case.cache, case.page_stride, case.block_table,
+                                      case.seq_lens, th.softmax_scale(), split_tokens=st)
     torch.cuda.synchronize()
-    tokens = [(0, 0), (5, 0)]
-    cache = th.oracle_cache(case, {b: range(case.ctx[b]) for b, _ in tokens})
-    ref_o, ref_l = th.oracle_dense(case, tokens=tokens, cache=cache)
-    worst, worst_lse = th.assert_parity(out, lse, ref_o, ref_l, tokens=tokens, what="dense")
-    print(f"dense: worst row err {worst:.2e} lse {worst_lse:.2e}", flush=True)
+    return case, runs
+
+
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_dense_146k_every_row(dense_run, part):
+    """Every output row of the dense configuration: tokens of requests 2*part and 2*part+1, for
+    both split sizes."""
+    case, runs = dense_run
+    for b in (2 * part, 2 * part + 1):
+        tokens = [(b, 0)]
+        cache = th.oracle_cache(case, {b: range(case.ctx[b])})
+        ref_o, ref_l = th.oracle_dense(case, tokens=tokens, cache=cache)
+        for st, (out, lse) in runs.items():
+            w = th.assert_parity(out, lse, ref_o, ref_l, tokens=tokens, what=f"dense request {b} split {st}")
+            print(f"dense request {b} split_tokens={st}: worst row err {w[0]:.2e} lse {w[1]:.2e}", flush=True)
 
 
 def test_mixed_serving_step():

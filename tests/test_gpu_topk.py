@@ -139,20 +139,17 @@ def test_topk_batched_shape_full_size():
     assert np.array_equal(got, tk.topk_indices(s, [143360] * 32, 1, 2048))
 
 
-def test_topk_mtp_shape_sampled_rows():
-    """16 requests x 15 query tokens of 149,504 positions (240 rows in one launch); 24 rows are
-    checked against the oracle, the rest for validity (ascending, in the window, full)."""
+def test_topk_mtp_shape_every_row():
+    """16 requests x 15 query tokens of 149,504 positions (240 rows in one launch), each request
+    with its own length; every row is compared with the oracle (the tie rule makes the selected
+    list unique)."""
     print("case: topk MTP shape 16 x 15 x 149504, k=2048", flush=True)
     rng = np.random.default_rng(7)
     n = 149504
     s = rng.standard_normal((16, 15, n)).astype(np.float32)
     lens = [n - 97 * b for b in range(16)]
     got = _run(s, lens, 15, 2048)
-    for b, t in [(b, t) for b in range(0, 16, 2) for t in (0, 7, 14)]:
-        nv = min(tk.visible_count(lens[b], 15, t), n)
-        assert np.array_equal(got[b, t], tk.select_topk(s[b, t], nv, 2048)), (b, t)
     for b in range(16):
         for t in range(15):
-            row = got[b, t]
-            nv = tk.visible_count(lens[b], 15, t)
-            assert (row >= 0).all() and (row < nv).all() and (np.diff(row) > 0).all(), (b, t)
+            nv = min(tk.visible_count(lens[b], 15, t), n)
+            assert np.array_equal(got[b, t], tk.select_topk(s[b, t], nv, 2048)), (b, t)
