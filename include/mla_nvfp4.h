@@ -138,6 +138,22 @@ mla_status mla_dense_decode(const void* q, mla_dtype q_dtype,
                             int32_t split_tokens, int32_t num_splits, float* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Allocation-free sparse decode, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Arguments, results
+ * and num_splits as mla_sparse_decode; the split partials live in a library-owned device array of
+ * mla_noalloc_scratch_bytes() bytes (32 MiB), one per GPU, held until the process ends. The call
+ * allocates nothing. It returns MLA_ERR_WORKSPACE when mla_decode_workspace_size(B*q_len, H,
+ * num_splits) exceeds that size (the library's own split choice needs at most about 17 MB).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two streams or
+ * two host threads) race and must not be issued. */
+size_t mla_noalloc_scratch_bytes(void);
+mla_status mla_sparse_decode_noalloc(const void* q, mla_dtype q_dtype,
+                                     const void* kv_cache, int64_t page_stride_bytes, int64_t cache_bytes,
+                                     const int32_t* block_table, int32_t max_pages,
+                                     const int32_t* topk_idx, int32_t topk,
+                                     int32_t B, int32_t q_len, int32_t H, float softmax_scale,
+                                     int32_t num_splits, float* out, float* lse, hipStream_t stream);
+
 /* ---- FP8 baseline and the staged path ------------------------------------------------------
  * Page section "Making room for low-latency decode": before the NVFP4 change a row held the 512
  * latent and the 64 rope values as FP8, 576 bytes. Section "Native NVFP4 sparse MLA decode

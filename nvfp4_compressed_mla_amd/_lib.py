@@ -49,6 +49,8 @@ EXPORTED = [
     "mla_check_sparse_indices",
     "mla_check_dense_tables",
     "mla_check_slots",
+    "mla_noalloc_scratch_bytes",
+    "mla_sparse_decode_noalloc",
 ]
 
 
@@ -131,6 +133,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_check_dense_tables.restype = ctypes.c_int
     lib.mla_check_slots.argtypes = [vp, i64, i64, i64, i64]
     lib.mla_check_slots.restype = ctypes.c_int
+    lib.mla_noalloc_scratch_bytes.argtypes = []
+    lib.mla_noalloc_scratch_bytes.restype = sz
+    lib.mla_sparse_decode_noalloc.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32,
+                                              i32, i32, f32, i32, vp, vp, vp]
+    lib.mla_sparse_decode_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 

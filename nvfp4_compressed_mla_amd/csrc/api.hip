@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mla_nvfp4.h"
@@ -691,6 +692,78 @@ mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_b
   return hip_status(mla::launch_dequantize_rows(kv_cache, page_stride_bytes, cache_bytes, slots, n,
                                                 out, stream),
                     "dequantize_rows launch");
+}
+
+}  // extern "C"
+
+// ---- allocation-free sparse decode -----------------------------------------------------------
+// For callers that cannot call hipMalloc (code under HIP graph capture, tight serving loops,
+// harnesses that forbid it). The split partials that mla_sparse_decode keeps in a caller-provided
+// workspace live here in `scratch`, a file-scope device array of kNoallocScratchBytes. Each GPU
+// the library runs on holds its own copy, at its own address, until the process ends; that
+// address is looked up once per device with hipGetSymbolAddress (in host code the array's name
+// is only a host-side stand-in) and kept. Every call on a GPU shares that GPU's array, so calls
+// that overlap on one GPU (two streams, two host threads) race on it. The decode kernels write
+// every partial they later read, so nothing in the array has to start at zero.
+namespace {
+
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;    // 32 MiB per GPU
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up on the first call on the device.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+mla_status mla_sparse_decode_noalloc(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                     int64_t page_stride_bytes, int64_t cache_bytes,
+                                     const int32_t* block_table, int32_t max_pages,
+                                     const int32_t* topk_idx, int32_t topk, int32_t B,
+                                     int32_t q_len, int32_t H, float softmax_scale,
+                                     int32_t num_splits, float* out, float* lse,
+                                     hipStream_t stream) {
+  size_t need = 0;
+  if (B >= 1 && q_len >= 1 && H >= 16 && num_splits >= 1 && (int64_t)B * q_len <= INT32_MAX) {
+    need = ws_bytes((int64_t)B * q_len, H, num_splits);
+    if (need > kNoallocScratchBytes)
+      return fail(MLA_ERR_WORKSPACE,
+                  "the allocation-free decode keeps its split partials in a %zu-byte scratch "
+                  "array; this call needs %zu bytes (fewer splits or query tokens per call)",
+                  kNoallocScratchBytes, need);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch address (hipGetSymbolAddress)");
+  }
+  // invalid shapes fall through to mla_sparse_decode's own argument checks
+  return mla_sparse_decode(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes, block_table,
+                           max_pages, topk_idx, topk, B, q_len, H, softmax_scale, num_splits, out,
+                           lse, ws, need > 0 ? kNoallocScratchBytes : 0, stream);
 }
 
 }  // extern "C"
