@@ -346,6 +346,62 @@ def topk_bench(dev, reps=20):
     return res
 
 
+# ---- indexer scores -> top-k -> decode (the pages' launch shape) ----------------------------------
+
+def indexer_chain(dev, reps=20, rot=4):
+    """The step before the path and the path: FP8 indexer scores of every visible position
+    (64 heads x 128 dims), top-2048 selection, then the fused NVFP4 decode over the selected
+    rows, at the pages' launch shape (one request, 15 query tokens, 149,504 positions, 16 heads).
+    Each stage graph-replayed on its own, then the three in one graph per step; `rot` rotations
+    of distinct indexer caches, queries and MLA queries."""
+    import torch
+    import nvfp4_compressed_mla_amd as m
+    from nvfp4_compressed_mla_amd import workloads as wl
+    B, q_len, H, n = 1, 15, 16, 149504
+    wk = SparseWorkload("pages_chain", B, q_len, H, [n], 2048, 0, rot, 1006, dev)
+    ix = [wl.gen_indexer(wk.cache.numel() // PAGE, B, q_len, 1106 + r, dev) for r in range(rot)]
+    seq = torch.full((B,), n, dtype=torch.int32, device=dev)
+    scores = [torch.zeros(B, q_len, n, dtype=torch.float32, device=dev) for _ in range(rot)]
+    ws = torch.empty(m.mla_topk_workspace_size(B * q_len, n, 2048), dtype=torch.uint8, device=dev)
+
+    def idx_fn(r):
+        c, q, w = ix[r % rot]
+        m.mla_indexer_scores(q, w, c, wl.INDEXER_PAGE_BYTES, wk.block_table, seq, n_max=n,
+                             out=scores[r % rot])
+
+    def topk_fn(r):
+        m.mla_topk_indices(scores[r % rot], seq, 2048, out=wk.idx[r % rot], workspace=ws)
+
+    def chain(r):
+        idx_fn(r)
+        topk_fn(r)
+        wk.decode(r % rot)
+
+    for r in range(rot):                      # lists of the real indexer scores for the decode
+        idx_fn(r)
+        topk_fn(r)
+    torch.cuda.synchronize()
+    wk.valid_pairs = [int((i >= 0).sum().item()) for i in wk.idx]
+    res = {}
+    for name, fn in (("indexer", idx_fn), ("topk", topk_fn), ("decode", lambda r: wk.decode(r % rot)),
+                     ("chain", chain)):
+        ms = time_steps(fn, rot, reps * rot, rot)
+        res[name + "_us"] = round(ms * 1e3, 2)
+    T = B * q_len
+    flops = T * n * 64 * 128 * 2
+    byt = (wk.cache.numel() // PAGE) * wl.INDEXER_PAGE_BYTES + T * 64 * (128 + 4) + T * n * 4
+    t_idx = res["indexer_us"] * 1e-6
+    res["indexer_fp8_TFLOPs"] = round(flops / t_idx / 1e12, 1)
+    res["indexer_mfma_frac_fp8"] = round(flops / t_idx / 5.0e15, 4)
+    res["indexer_GBps"] = round(byt / t_idx / 1e9, 1)
+    res["indexer_hbm_frac"] = round(byt / t_idx / 8e12, 4)
+    res["note"] = ("indexer: 64 heads x 128 dims E4M3, MFMA-bound (36.7 GFLOP, 28.8 MB per launch); "
+                   "chain: indexer + top-k + decode captured together per step")
+    del wk, ix, scores
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---- block transfer between multi-layer pools --------------------------------------------------
 
 def kv_transfer(dev, n_layers=64, ctx=204800, pool_blocks=16000, reps=5):
@@ -540,7 +596,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--extras", default="all",
                     help="comma list of other configurations to run: pages, mtp, tiny, dense, "
-                         "mixed, three_way, mtp_overlap, kv_transfer, topk, ceiling, flush (default all; 'none' = --no-extra)")
+                         "mixed, three_way, mtp_overlap, kv_transfer, topk, indexer, ceiling, flush (default all; 'none' = --no-extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -650,7 +706,7 @@ def main():
     }
 
     wanted = set() if args.no_extra or args.extras == "none" else (
-        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk",
+        {"pages", "mtp", "tiny", "dense", "mixed", "three_way", "mtp_overlap", "kv_transfer", "topk", "indexer",
          "ceiling", "flush"} if args.extras == "all"
         else set(args.extras.split(",")))
     if wanted:
@@ -745,6 +801,9 @@ def main():
             extra["mtp_overlap_B16_q15_H64"] = ov
         if "topk" in wanted:
             extra["topk_2048"] = topk_bench(dev)
+        if "indexer" in wanted:
+            log("[bench] extra: indexer -> top-k -> decode chain")
+            extra["indexer_chain_T15_H16_146K"] = indexer_chain(dev)
         if "kv_transfer" in wanted:
             extra["kv_transfer_200K"] = kv_transfer(dev)
         if "flush" in wanted:

@@ -65,6 +65,9 @@ typedef enum { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
 #define MLA_PAGE_ROWS 64
 #define MLA_MAX_TOPK 2048
 #define MLA_FP8_ROW_BYTES 576
+#define MLA_INDEXER_HEADS 64
+#define MLA_INDEXER_DIM 128
+#define MLA_INDEXER_PAGE_BYTES 8448   /* 64 E4M3 keys of 128 bytes, then 64 fp32 scales */
 
 /* Quantize-on-append (page section "Making room for low-latency decode": the latent is stored
  * as NVFP4, the rope part as FP8).
@@ -266,6 +269,33 @@ size_t mla_topk_workspace_size(int32_t num_tokens, int64_t n_max, int32_t k);
 mla_status mla_topk_indices(const float* scores, int64_t n_max, const int32_t* seq_lens,
                             int32_t B, int32_t q_len, int32_t k, int32_t* out_idx,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Indexer scores (the FP8 scoring pass that top-k selects from) ------------------------------
+ * Page section "Native NVFP4 sparse MLA decode kernel": attention reads the positions a sparse
+ * indexer selected; section "Making room for low-latency decode" keeps the indexer's cache beside
+ * the MLA rows. The page does not define the indexer's scores. This library's reading (synthetic
+ * inputs, no trained weights): position s holds a 128-dim E4M3 key k_s and a positive fp32 scale
+ * c_s; query token t has 64 E4M3 heads q_{t,j} and fp32 head weights w_{t,j};
+ *     scores[t, s] = c_s * sum_j w_{t,j} * max(0, q_{t,j} . k_s)
+ * accumulated in fp32 (E4M3 products are exact).
+ *   q_fp8        E4M3 bytes [B, q_len, 64, 128], 16-byte aligned.
+ *   head_weights fp32 [B, q_len, 64], 16-byte aligned.
+ *   k_cache      indexer pages: page p at k_cache + p*page_stride_bytes holds the keys of its 64
+ *                positions (128 bytes each) and then their 64 fp32 scales; page_stride_bytes >=
+ *                MLA_INDEXER_PAGE_BYTES, a multiple of 16; cache_bytes as for the MLA cache.
+ *   block_table  int32 [B, max_pages]: position s of request b lives in page block_table[b][s/64]
+ *                (the same table as the MLA rows; an unmapped or out-of-cache page scores as 0).
+ *   seq_lens     int32 [B]; token t scores positions 0 .. seq_lens[b] - q_len + t (clamped to
+ *                n_max and max_pages*64), the window mla_topk_indices selects from.
+ *   scores       fp32 [B, q_len, n_max]: those positions are written; the rest are left as they
+ *                are. 1 <= n_max <= 1,048,576; B <= 65,535.
+ * Errors: MLA_ERR_INVALID_ARG for null or misaligned pointers and sizes out of range (checked on
+ * the host, before any launch). */
+mla_status mla_indexer_scores(const void* q_fp8, const float* head_weights, const void* k_cache,
+                              int64_t page_stride_bytes, int64_t cache_bytes,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t B, int32_t q_len, int64_t n_max,
+                              float* scores, hipStream_t stream);
 
 /* Test hook, off the hot path: decode the rows at `slots` (int64 [n]) into fp32 [n, 576]
  * (latent then rope), through the same on-chip decoder the attention kernels use. Values are

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     mla_fp8_append,
     mla_fp8_dense_decode,
     mla_fp8_sparse_decode,
+    mla_indexer_scores,
     mla_kv_transfer_regions,
     mla_nvfp4_dequantize_rows,
     mla_nvfp4_quantize_append,

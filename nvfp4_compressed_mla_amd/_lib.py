@@ -41,6 +41,7 @@ EXPORTED = [
     "mla_kv_transfer_regions",
     "mla_topk_workspace_size",
     "mla_topk_indices",
+    "mla_indexer_scores",
     "mla_set_timing_events",
     "mla_status_string",
     "mla_last_error",
@@ -117,6 +118,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_topk_workspace_size.restype = sz
     lib.mla_topk_indices.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
     lib.mla_topk_indices.restype = ctypes.c_int
+    lib.mla_indexer_scores.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp, i32, i32, i64, vp, vp]
+    lib.mla_indexer_scores.restype = ctypes.c_int
     lib.mla_set_timing_events.argtypes = [vp, vp]
     lib.mla_set_timing_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -478,6 +481,44 @@ def mla_topk_indices(scores, seq_lens, k: int, out=None, workspace=None, stream=
     _check(load_library().mla_topk_indices(
         _ptr(scores), n_max, _ptr(seq_lens), B, q_len, int(k), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+    return out
+
+
+INDEXER_HEADS = 64
+INDEXER_DIM = 128
+INDEXER_PAGE_BYTES = 8448
+
+
+def mla_indexer_scores(q_fp8, head_weights, k_cache, page_stride: int, block_table, seq_lens,
+                       n_max: int = None, out=None, stream=None):
+    """FP8 indexer scores [B, q_len, n_max] (fp32): q_fp8 uint8 [B, q_len, 64, 128] (E4M3 bytes),
+    head_weights fp32 [B, q_len, 64], k_cache uint8 indexer pages (64 keys of 128 bytes, then 64
+    fp32 scales per page). Positions a token may not select are left as they are in ``out``."""
+    torch = _torch()
+    _require(q_fp8, "q_fp8", torch.uint8)
+    _require(head_weights, "head_weights", torch.float32)
+    _require(k_cache, "k_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    if q_fp8.dim() != 4 or q_fp8.shape[2:] != (INDEXER_HEADS, INDEXER_DIM) or not q_fp8.is_contiguous():
+        raise ValueError("q_fp8 must be contiguous uint8 [B, q_len, 64, 128]")
+    B, q_len = q_fp8.shape[:2]
+    if head_weights.shape != (B, q_len, INDEXER_HEADS) or not head_weights.is_contiguous():
+        raise ValueError("head_weights must be contiguous fp32 [B, q_len, 64]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    if n_max is None:
+        n_max = block_table.shape[1] * 64
+    if out is None:
+        out = torch.zeros(B, q_len, n_max, dtype=torch.float32, device=q_fp8.device)
+    elif out.shape != (B, q_len, n_max) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, q_len, n_max]")
+    _check(load_library().mla_indexer_scores(
+        _ptr(q_fp8), _ptr(head_weights), _ptr(k_cache), int(page_stride), k_cache.numel(),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, q_len, int(n_max), _ptr(out),
+        _stream(stream)))
     return out
 
 

@@ -680,6 +680,45 @@ mla_status mla_topk_indices(const float* scores, int64_t n_max, const int32_t* s
                     "topk launch");
 }
 
+mla_status mla_indexer_scores(const void* q_fp8, const float* head_weights, const void* k_cache,
+                              int64_t page_stride_bytes, int64_t cache_bytes,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t B, int32_t q_len, int64_t n_max,
+                              float* scores, hipStream_t stream) {
+  if (!q_fp8 || !head_weights || !block_table || !seq_lens || !scores)
+    return fail(MLA_ERR_INVALID_ARG, "null q_fp8 / head_weights / block_table / seq_lens / scores");
+  if (!k_cache) return fail(MLA_ERR_INVALID_ARG, "k_cache is null");
+  if (!aligned(k_cache, 16)) return fail(MLA_ERR_INVALID_ARG, "k_cache must be 16-byte aligned");
+  if (page_stride_bytes < MLA_INDEXER_PAGE_BYTES || page_stride_bytes % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_stride_bytes %lld must be >= %d and a multiple of 16",
+                (long long)page_stride_bytes, MLA_INDEXER_PAGE_BYTES);
+  if (cache_bytes < MLA_INDEXER_PAGE_BYTES || cache_bytes > kMaxCacheBytes)
+    return fail(MLA_ERR_INVALID_ARG, "cache_bytes %lld out of range", (long long)cache_bytes);
+  if (B < 1 || B > 65535 || q_len < 1) return fail(MLA_ERR_INVALID_ARG, "B must be in [1, 65535], q_len >= 1");
+  if (max_pages < 1) return fail(MLA_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (n_max < 1 || n_max > mla::kTopkMaxN)
+    return fail(MLA_ERR_INVALID_ARG, "n_max %lld outside [1, %lld]", (long long)n_max, (long long)mla::kTopkMaxN);
+  if ((int64_t)B * q_len > (int64_t)1 << 20) return fail(MLA_ERR_INVALID_ARG, "too many query tokens");
+  if (!aligned(q_fp8, 16) || !aligned(head_weights, 16))
+    return fail(MLA_ERR_INVALID_ARG, "q_fp8 and head_weights must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(scores, 4))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned block_table / seq_lens / scores");
+  mla::IndexerArgs a;
+  a.q = (const uint8_t*)q_fp8;
+  a.weights = head_weights;
+  a.cache = (const uint8_t*)k_cache;
+  a.page_stride = page_stride_bytes;
+  a.cache_bytes = cache_bytes;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.q_len = q_len;
+  a.n_max = n_max;
+  a.scores = scores;
+  return hip_status(mla::launch_indexer(a, stream), "indexer launch");
+}
+
 mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_bytes,
                                      int64_t cache_bytes, const int64_t* slots, int64_t n,
                                      float* out, hipStream_t stream) {

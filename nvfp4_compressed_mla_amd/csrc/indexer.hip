@@ -1,0 +1,164 @@
+// Indexer scores: the FP8 scoring pass that feeds top-k position selection.
+//
+// Page "Prime Inference: Fast, Reliable Serving for Frontier Open Models", section "Native NVFP4
+// sparse MLA decode kernel": the decode reads the positions a sparse indexer selected, 2048 per
+// query token (section "Decode: NVFP4 KV compression"); section "Making room for low-latency
+// decode" keeps the indexer's own cache state unchanged beside the compressed MLA rows. The page
+// does not define the indexer's scoring function. The reading implemented here (synthetic, no
+// trained weights): every position s holds a 128-dim E4M3 indexer key k_s with a positive fp32
+// scale c_s; query token t has 64 E4M3 indexer heads q_{t,j} (128 dims) and fp32 head weights
+// w_{t,j}; the score is
+//     score[t, s] = c_s * sum_j w_{t,j} * max(0, q_{t,j} . k_s).
+// Token t of a request with seq_len positions and q_len query tokens scores positions
+// 0 .. seq_len - q_len + t (the causal window the top-k step selects from).
+//
+// Indexer cache page (64 positions, MLA_INDEXER_PAGE_BYTES = 8448): 64 keys of 128 bytes, then 64
+// fp32 scales. Pages are found through the request's block table, as the MLA rows are.
+//
+// MI355X design. One workgroup (8 waves) per (request, block of at most 512 positions, sized
+// so that one launch fills two workgroups per CU); two workgroups per CU. The block's keys are staged once in LDS (64 KB, 16-byte pieces XOR-swizzled by row so
+// that the operand reads are free of bank conflicts) and reused by every query token of the
+// request: wave w scores tokens w, w+8, ... Per token the wave holds the queries of the 64 heads
+// as four A operands (32 VGPRs) and runs v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit
+// block scales, FP32 accumulation: the whole 128-dim dot product in one instruction) over
+// 16-position tiles, two tiles (8 independent MFMAs) at a time: a lane then holds 4 heads of one
+// position per MFMA, applies the ReLU and the head weights, and the four lane groups are summed
+// with lane swaps. Products of two E4M3 values
+// are exact in FP32, so the only rounding is the FP32 accumulation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+#include "nvfp4_device.h"
+
+namespace mla {
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kIdxThreads = 512;
+constexpr int kIdxWaves = kIdxThreads / 64;
+constexpr int kIdxBlockRows = 512;                      // positions per workgroup, at most
+constexpr int kIdxScaleOff = kPageRows * kIndexerDim;   // 8192: scales after the keys
+
+__device__ __forceinline__ float idx_group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerArgs a) {
+  // key r, 16-byte piece c (dims 16c..16c+15) at r*128 + 16*(c ^ (r & 7))
+  __shared__ __attribute__((aligned(16))) uint8_t keys[kIdxBlockRows * kIndexerDim];
+  __shared__ float kscale[kIdxBlockRows];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int b = blockIdx.y;
+  const int p0 = blockIdx.x * a.block_rows;
+  const int64_t n_cols = min((int64_t)a.n_max, (int64_t)a.max_pages * kPageRows);
+  const int n_pos = (int)min((int64_t)a.seq_lens[b], n_cols);     // positions any token may see
+  if (p0 >= n_pos) return;
+  const int rows = min(a.block_rows, n_pos - p0);
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  // ---- stage the block's keys and scales (an unmapped or out-of-cache page reads as zeros) ----
+  {
+    const int c = tid & 7;
+#pragma unroll 4
+    for (int i = 0; i < kIdxBlockRows * 8 / kIdxThreads; ++i) {
+      const int r = (tid >> 3) + (kIdxThreads / 8) * i;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows) {
+        const int pos = p0 + r;
+        const int pg = bt[pos >> 6];
+        const int64_t off = (int64_t)pg * a.page_stride;
+        if (pg >= 0 && off + kIndexerPageBytes <= a.cache_bytes)
+          v = *(const uint4*)(a.cache + off + (int64_t)(pos & 63) * kIndexerDim + 16 * c);
+      }
+      *(uint4*)(keys + r * kIndexerDim + ((c ^ (r & 7)) << 4)) = v;
+    }
+    for (int r = tid; r < kIdxBlockRows; r += kIdxThreads) {
+      float s = 0.0f;
+      if (r < rows) {
+        const int pos = p0 + r;
+        const int pg = bt[pos >> 6];
+        const int64_t off = (int64_t)pg * a.page_stride;
+        if (pg >= 0 && off + kIndexerPageBytes <= a.cache_bytes)
+          s = *(const float*)(a.cache + off + kIdxScaleOff + 4 * (pos & 63));
+      }
+      kscale[r] = s;
+    }
+  }
+  __syncthreads();
+
+  // ---- score: wave w takes query tokens w, w+8, ... ------------------------------------------
+  for (int t = w; t < a.q_len; t += kIdxWaves) {
+    const int64_t tok = (int64_t)b * a.q_len + t;
+    const int vis = min(a.seq_lens[b] - a.q_len + 1 + t, n_pos);   // positions 0 .. vis-1
+    const int nr = min(vis - p0, a.block_rows);
+    if (nr <= 0) continue;
+    // A operands: lane (l16, kg) holds dims 32*kg .. 32*kg+31 of head 16*hb + l16; the B
+    // operands (keys) below use the same lane -> dims map, so the MFMA sums all 128 dims.
+    i32x8 qa[4];
+    f32x4 wv[4];                               // weights of heads 16*hb + 4*kg + e (output rows)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const uint4* src = (const uint4*)(a.q + (tok * kIndexerHeads + 16 * hb + l16) * kIndexerDim + 32 * kg);
+      const uint4 lo = src[0], hi = src[1];
+      qa[hb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      wv[hb] = *(const f32x4*)(a.weights + tok * kIndexerHeads + 16 * hb + 4 * kg);
+    }
+    // The row's visible part as a buffer resource (0x00020000: raw 32-bit dwords on gfx9): the
+    // hardware drops stores at offsets past nr positions, so the epilogue needs no branch.
+    const __amdgpu_buffer_rsrc_t out_rs =
+        __builtin_amdgcn_make_buffer_rsrc(a.scores + tok * a.n_max + p0, (short)0, nr * 4, 0x00020000);
+    const int n_kt = (nr + 15) >> 4;
+    // two 16-position tiles per step: 8 independent MFMAs, then their epilogues
+    for (int kt0 = 0; kt0 < n_kt; kt0 += 2) {
+      f32x4 d[2][4];
+      int rr[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        rr[u] = min((kt0 + u) * 16 + l16, kIdxBlockRows - 1);    // (a tile past n_kt is not stored)
+        const uint8_t* kr = keys + rr[u] * kIndexerDim;
+        const uint4 k0 = *(const uint4*)(kr + (((2 * kg) ^ (rr[u] & 7)) << 4));
+        const uint4 k1 = *(const uint4*)(kr + (((2 * kg + 1) ^ (rr[u] & 7)) << 4));
+        const i32x8 kb = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          // E4M3 x E4M3 (format 0 for both operands), E8M0 block scales 127 = 1.0
+          d[u][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[hb], kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float sh[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          sh[hb] = wv[hb][0] * fmaxf(d[u][hb][0], 0.0f);
+#pragma unroll
+          for (int e = 1; e < 4; ++e) sh[hb] = __builtin_fmaf(wv[hb][e], fmaxf(d[u][hb][e], 0.0f), sh[hb]);
+        }
+        const float s = idx_group4_sum((sh[0] + sh[1]) + (sh[2] + sh[3])) * kscale[rr[u]];
+        const int r = (kt0 + u) * 16 + l16;
+        // one lane group stores (the others hold the same sum); offsets past the row are dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), out_rs, kg == 0 ? 4 * r : 0x7FFFFFF0, 0, 0);
+      }
+    }
+  }
+}
+
+hipError_t launch_indexer(const IndexerArgs& a_in, hipStream_t stream) {
+  IndexerArgs a = a_in;
+  const int64_t n_cols = std::min<int64_t>(a.n_max, (int64_t)a.max_pages * kPageRows);
+  // positions per workgroup: a multiple of 64, at most 512, and small enough that the launch
+  // fills the two workgroup slots of every CU when it can (512 workgroups)
+  const int64_t per = ((int64_t)a.B * n_cols + 511) / 512;
+  a.block_rows = (int32_t)std::min<int64_t>(kIdxBlockRows, std::max<int64_t>(64, (per + 63) / 64 * 64));
+  const dim3 grid((unsigned)((n_cols + a.block_rows - 1) / a.block_rows), (unsigned)a.B);
+  hipLaunchKernelGGL(indexer_kernel, grid, dim3(kIdxThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

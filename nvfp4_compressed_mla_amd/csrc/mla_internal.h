@@ -101,4 +101,24 @@ inline size_t topk_ws_bytes(int64_t T, int64_t n_max, int64_t /*k*/) {
 hipError_t launch_topk(const float* scores, int64_t n_max, const int32_t* seq_lens, int32_t T,
                        int32_t q_len, int32_t k, void* workspace, int32_t* out, hipStream_t stream);
 
+// Indexer scoring pass (FP8 scores of every visible position, the input of top-k selection).
+constexpr int kIndexerHeads = 64;
+constexpr int kIndexerDim = 128;
+constexpr int kIndexerPageBytes = 64 * kIndexerDim + 64 * 4;   // 64 E4M3 keys, 64 fp32 scales
+struct IndexerArgs {
+  const uint8_t* q;            // [T, 64, 128] E4M3 indexer queries, T = B*q_len
+  const float* weights;        // [T, 64] head weights
+  const uint8_t* cache;        // indexer pages
+  int64_t page_stride;         // bytes
+  int64_t cache_bytes;
+  const int32_t* block_table;  // [B, max_pages]
+  int32_t max_pages;
+  const int32_t* seq_lens;     // [B]
+  int32_t B, q_len;
+  int64_t n_max;
+  float* scores;               // [T, n_max]; visible positions written
+  int32_t block_rows;          // positions per workgroup (set by launch_indexer)
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
+
 }  // namespace mla

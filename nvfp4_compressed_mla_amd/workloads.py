@@ -16,7 +16,9 @@ Distributions: latent, rope and queries ~ N(0, 1) (bf16; fp32 queries for the ti
 tables are a random permutation of all physical pages, sliced per request; top-k lists are the
 first k entries of an argsort of uniform keys (uniform sampling without replacement), drawn
 independently per query token; when a context is shorter than k the list holds every position
-once and the remaining entries are -1, scattered at random places in the list.
+once and the remaining entries are -1, scattered at random places in the list. Indexer inputs
+(the synthetic FP8 scorer the top-k step reads): keys and queries are N(0, 1) values cast to
+E4M3, key scales uniform in [0.5, 1.5), head weights N(0, 1) / 8.
 """
 
 from __future__ import annotations
@@ -179,3 +181,28 @@ def gen_topk_batched(B: int, q_len: int, k: int, ctx: int, seed: int, device="cp
     keys = torch.rand(B * q_len, ctx, generator=g, device=device)
     idx = torch.topk(keys, k, dim=1, largest=False, sorted=False).indices
     return idx.to(torch.int32).reshape(B, q_len, k)
+
+
+INDEXER_HEADS = 64
+INDEXER_DIM = 128
+INDEXER_PAGE_BYTES = 64 * INDEXER_DIM + 64 * 4
+
+
+def gen_indexer(n_pages: int, B: int, q_len: int, seed: int, device="cpu"):
+    """Synthetic indexer inputs (no trained weights): an indexer cache of ``n_pages`` pages (64
+    keys of 128 E4M3 bytes, then 64 fp32 scales, per page), queries of 64 heads x 128 dims as
+    E4M3 bytes [B, q_len, 64, 128] and fp32 head weights [B, q_len, 64].
+
+    Keys and queries are N(0, 1) values cast to E4M3 by torch (round to nearest); key scales are
+    uniform in [0.5, 1.5); head weights are N(0, 1) / 8. Drawn on the host, moved with one copy
+    each. Returns (k_cache uint8 [n_pages * 8448], q_fp8, weights).
+    """
+    g = _gen(seed, "cpu")
+    keys = torch.randn(n_pages * 64, INDEXER_DIM, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = (0.5 + torch.rand(n_pages * 64, generator=g)).to(torch.float32)
+    page = torch.empty(n_pages, INDEXER_PAGE_BYTES, dtype=torch.uint8)
+    page[:, :64 * INDEXER_DIM] = keys.reshape(n_pages, 64 * INDEXER_DIM)
+    page[:, 64 * INDEXER_DIM:] = scales.reshape(n_pages, 64).view(torch.uint8).reshape(n_pages, 256)
+    q = torch.randn(B, q_len, INDEXER_HEADS, INDEXER_DIM, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+    w = torch.randn(B, q_len, INDEXER_HEADS, generator=g) / 8.0
+    return page.reshape(-1).to(device), q.contiguous().to(device), w.contiguous().to(device)

@@ -24,9 +24,9 @@ Modules: ``nvfp4`` (element and row codec), ``fp8`` (the 576-byte FP8 baseline r
 NVFP4 -> FP8 conversion), ``cache`` (paged row addressing), ``attention`` (fp64 sparse / dense
 absorbed-MLA decode and the split log-sum-exp merge), ``layout`` (block-major and layer-major
 multi-layer page layouts, transfer regions, block copy), ``topk`` (top-k selection of positions
-from per-position scores).
+from per-position scores), ``indexer`` (the FP8 indexer scores top-k selects from).
 
 Parity pins live in ``tests/test_oracle_*.py`` (run with ``-m "not gpu"``).
 """
 
-from . import nvfp4, fp8, cache, attention, layout, topk  # noqa: F401
+from . import nvfp4, fp8, cache, attention, layout, topk, indexer  # noqa: F401
