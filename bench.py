@@ -119,8 +119,22 @@ class SparseWorkload:
         self.valid_pairs = [int((i >= 0).sum().item()) for i in self.idx]
         torch.cuda.synchronize()
 
+    def use_shared_rows(self):
+        """Decode through the shared-row entry point from now on (same inputs and result)."""
+        import torch
+        import nvfp4_compressed_mla_amd as m
+        need = m.mla_shared_decode_workspace_size(self.B, self.q_len, self.H, self.topk)
+        self.ws_shared = torch.empty(max(need, 256), dtype=torch.uint8, device=self.cache.device)
+        self.splits = m.mla_shared_decode_num_splits(self.B, self.q_len, self.H, self.topk)
+        self.fmt = "shared"
+
     def decode(self, r):
         import nvfp4_compressed_mla_amd as m
+        if self.fmt == "shared":
+            m.mla_sparse_decode_shared(self.q[r], self.cache, self.page, self.block_table, self.idx[r],
+                                       1.0 / math.sqrt(576.0), out=self.out, lse=self.lse,
+                                       workspace=self.ws_shared)
+            return
         fn = {"nvfp4": m.mla_sparse_decode, "fp8": m.mla_fp8_sparse_decode,
               "staged": m.mla_staged_sparse_decode}[self.fmt]
         fn(self.q[r], self.cache, self.page, self.block_table, self.idx[r], 1.0 / math.sqrt(576.0),
@@ -799,6 +813,25 @@ def main():
                 del w2
                 torch.cuda.empty_cache()
             extra["mtp_overlap_B16_q15_H64"] = ov
+            # 16 heads per token (the pages' per-rank head count): per-token launch against the
+            # shared-row path (each distinct row of 4 consecutive tokens gathered and decoded once)
+            ov16 = {}
+            for f in (0.0, 0.5, 0.9):
+                log(f"[bench] extra: mtp_overlap H=16 {f}")
+                w3 = SparseWorkload("mtp_ov16", 16, 15, 16, [149504] * 16, 2048, 0, 6, 1007, dev, overlap=f)
+                res = {"per_token": run_config(w3, 192, 24, 32)}
+                w3.use_shared_rows()
+                res["shared_rows"] = run_config(w3, 192, 24, 32)
+                res["shared_rows"]["note"] = ("fused_kernel_us: the shared decode kernel alone; "
+                                              "us_per_launch adds the union pass and the split merge; "
+                                              "bytes and flops counted per (token, row) pair as in "
+                                              "per_token")
+                uniq = [len(set(w3.idx[0][b].flatten().tolist())) for b in range(16)]
+                res["distinct_rows_per_request"] = round(sum(uniq) / len(uniq), 1)
+                ov16[f"overlap_{f}"] = res
+                del w3
+                torch.cuda.empty_cache()
+            extra["mtp_overlap_B16_q15_H16"] = ov16
         if "topk" in wanted:
             extra["topk_2048"] = topk_bench(dev)
         if "indexer" in wanted:

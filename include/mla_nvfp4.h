@@ -129,6 +129,32 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype,
                              int32_t num_splits, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Sparse decode with rows shared across query tokens (page section "Native NVFP4 sparse MLA
+ * decode kernel": a launch carries several query tokens of a request, 15 in the page's figure).
+ * Same arguments and result as mla_sparse_decode; the work is split differently: the lists of
+ * each group of up to 4 consecutive query tokens of a request are merged into their union
+ * (distinct positions, ascending, with a 4-bit mask of the tokens that selected each), and one
+ * workgroup serves 16 heads of each of the group's tokens over that union, gathering and
+ * decoding each distinct row once and masking, per token, the rows it did not select. Pays when
+ * the tokens' lists overlap (the union is much shorter than the lists together) and the
+ * per-token launch is compute-bound, e.g. 16 heads per token; at 64 heads every tile already
+ * serves 64 query rows, and the plain entry point is faster.
+ * Requirements beyond mla_sparse_decode's: max_pages*64 <= 1,048,576 (the union is built over
+ * the request's positions in on-chip memory, in 16 position ranges), and no position twice in one
+ * token's list (a repeated position counts once here, twice in mla_sparse_decode).
+ *   workspace  mla_shared_decode_workspace_size(B, q_len, H, topk) bytes, 256-byte aligned:
+ *              union lists, masks and sizes, then the split partials.
+ * Launches: the union pass, the decode, then the split merge when
+ * mla_shared_decode_num_splits(...) > 1. Deterministic. */
+size_t mla_shared_decode_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t topk);
+int32_t mla_shared_decode_num_splits(int32_t B, int32_t q_len, int32_t H, int32_t topk);
+mla_status mla_sparse_decode_shared(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                                    int32_t H, float softmax_scale, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Dense decode over the whole cache of each request (no indexer): query token t of request b
  * attends to logical positions 0 .. seq_lens[b]-q_len+t (causal inside the step), split into
  * chunks of split_tokens positions (a multiple of 64, at most 8192) merged by log-sum-exp.

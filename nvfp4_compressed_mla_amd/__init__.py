@@ -28,7 +28,10 @@ from ._lib import (  # noqa: F401
     mla_nvfp4_stage_fp8,
     mla_set_debug_checks,
     mla_set_timing_events,
+    mla_shared_decode_num_splits,
+    mla_shared_decode_workspace_size,
     mla_sparse_decode,
+    mla_sparse_decode_shared,
     mla_sparse_decode_num_splits,
     mla_staged_sparse_decode,
     mla_staged_workspace_size,

@@ -29,6 +29,9 @@ EXPORTED = [
     "mla_dense_decode_num_splits",
     "mla_dense_decode_split_tokens",
     "mla_sparse_decode",
+    "mla_shared_decode_workspace_size",
+    "mla_shared_decode_num_splits",
+    "mla_sparse_decode_shared",
     "mla_dense_decode",
     "mla_nvfp4_dequantize_rows",
     "mla_fp8_append",
@@ -93,6 +96,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_sparse_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
                                       i32, f32, i32, vp, vp, vp, sz, vp]
     lib.mla_sparse_decode.restype = ctypes.c_int
+    lib.mla_shared_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.mla_shared_decode_workspace_size.restype = sz
+    lib.mla_shared_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    lib.mla_shared_decode_num_splits.restype = i32
+    lib.mla_sparse_decode_shared.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32,
+                                             i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.mla_sparse_decode_shared.restype = ctypes.c_int
     lib.mla_dense_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
                                      f32, i32, i32, vp, vp, vp, sz, vp]
     lib.mla_dense_decode.restype = ctypes.c_int
@@ -275,6 +285,43 @@ def mla_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, sof
     """
     return _sparse("mla_sparse_decode", q, kv_cache, page_stride_bytes, block_table, topk_idx,
                    softmax_scale, out, lse, num_splits, workspace, want_lse, stream)
+
+
+def mla_shared_decode_workspace_size(B: int, q_len: int, H: int, topk: int) -> int:
+    return int(load_library().mla_shared_decode_workspace_size(B, q_len, H, topk))
+
+
+def mla_shared_decode_num_splits(B: int, q_len: int, H: int, topk: int) -> int:
+    return int(load_library().mla_shared_decode_num_splits(B, q_len, H, topk))
+
+
+def mla_sparse_decode_shared(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,
+                             out=None, lse=None, workspace=None, want_lse=True, stream=None):
+    """Sparse decode with each distinct row of a group of up to 4 consecutive query tokens
+    gathered and decoded once (same result as ``mla_sparse_decode``); returns (out, lse)."""
+    torch = _torch()
+    _require(q, "q")
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(topk_idx, "topk_idx", torch.int32)
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, q_len, H, 576]")
+    B, q_len, H, _ = q.shape
+    if topk_idx.dim() != 3 or tuple(topk_idx.shape[:2]) != (B, q_len) or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous int32 [B, q_len, topk]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    topk = topk_idx.shape[2]
+    out, lse = _outputs(q, out, lse, want_lse)
+    need = mla_shared_decode_workspace_size(B, q_len, H, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    _check(load_library().mla_sparse_decode_shared(
+        _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
+        _ptr(block_table), block_table.shape[1], _ptr(topk_idx), topk, B, q_len, H,
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out, lse
 
 
 def mla_fp8_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,

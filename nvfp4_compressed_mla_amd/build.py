@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_nvfp4.so")
-SOURCES = ["api.hip", "codec.hip", "decode.hip", "fp8.hip", "indexer.hip", "layout.hip", "topk.hip"]
+SOURCES = ["api.hip", "codec.hip", "decode.hip", "fp8.hip", "indexer.hip", "layout.hip", "topk.hip", "union.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

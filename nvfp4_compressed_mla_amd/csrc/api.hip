@@ -454,6 +454,33 @@ StagedLayout staged_layout(int64_t T, int32_t H, int32_t topk, int32_t num_split
   return l;
 }
 
+// Shared-row decode workspace: union positions, token masks, union sizes, split partials.
+struct SharedLayout {
+  int32_t groups, stride, S;
+  size_t mask, count, part, total;
+};
+
+SharedLayout shared_layout(int32_t B, int32_t q_len, int32_t H, int32_t topk) {
+  SharedLayout l;
+  l.groups = B * ((q_len + 3) / 4);
+  l.stride = 4 * topk;
+  // at least enough splits to keep every split's share of a union within the row list a
+  // workgroup holds, then enough to fill ~90% of one wave of workgroups (at most 16)
+  const int32_t min_s = (4 * topk + mla::kMaxSplitRows - 1) / mla::kMaxSplitRows;
+  const int64_t items = (int64_t)l.groups * (H / 16);
+  int64_t s = (kComputeUnits * 9 / 10 + items - 1) / items;
+  if (s > 16) s = 16;
+  if (s < min_s) s = min_s;
+  if (s < 1) s = 1;
+  l.S = (int32_t)s;
+  const size_t n = (size_t)l.groups * mla::kUnionParts * (size_t)l.stride;
+  l.mask = round256(n * sizeof(int32_t));
+  l.count = l.mask + round256(n);
+  l.part = l.count + round256((size_t)l.groups * mla::kUnionParts * sizeof(int32_t));
+  l.total = l.part + ws_bytes((int64_t)B * q_len, H, l.S);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +495,98 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_ca
   return sparse_decode_impl(false, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
                             block_table, max_pages, topk_idx, topk, B, q_len, H, softmax_scale,
                             num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t mla_shared_decode_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t topk) {
+  if (B < 1 || q_len < 1 || H < 16 || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  return shared_layout(B, q_len, H, topk).total;
+}
+
+int32_t mla_shared_decode_num_splits(int32_t B, int32_t q_len, int32_t H, int32_t topk) {
+  if (B < 1 || q_len < 1 || H < 16 || topk < 1 || topk > MLA_MAX_TOPK) return 1;
+  return shared_layout(B, q_len, H, topk).S;
+}
+
+mla_status mla_sparse_decode_shared(const void* q, mla_dtype q_dtype, const void* kv_cache,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                                    int32_t H, float softmax_scale, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                                      block_table, max_pages, B, q_len, H, softmax_scale, 1, out,
+                                      lse, nullptr, 0);
+  if (st != MLA_OK) return st;
+  if (!topk_idx) return fail(MLA_ERR_INVALID_ARG, "topk_idx is null");
+  if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
+  if (!aligned(topk_idx, 4) || !aligned(block_table, 4)) return fail(MLA_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  if ((int64_t)max_pages * MLA_PAGE_ROWS > mla::kUnionMaxPos)
+    return fail(MLA_ERR_UNSUPPORTED, "shared rows: max_pages*64 = %lld positions > %d",
+                (long long)max_pages * MLA_PAGE_ROWS, mla::kUnionMaxPos);
+  const SharedLayout l = shared_layout(B, q_len, H, topk);
+  if ((int64_t)l.groups * (H / 16) * l.S > (int64_t)1 << 28) return fail(MLA_ERR_INVALID_ARG, "launch too large");
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed", l.total);
+  if (debug_checks_on()) {
+    const int64_t T = (int64_t)B * q_len;
+    std::vector<int32_t> hi, hb;
+    if ((st = debug_copy(hi, topk_idx, (size_t)(T * topk), stream, "topk_idx")) != MLA_OK) return st;
+    if ((st = debug_copy(hb, block_table, (size_t)B * max_pages, stream, "block_table")) != MLA_OK) return st;
+    st = mla_check_sparse_indices(hi.data(), B, q_len, topk, hb.data(), max_pages, page_stride_bytes,
+                                  cache_bytes, MLA_ROW_BYTES);
+    if (st != MLA_OK) return st;
+  }
+  uint8_t* ws = (uint8_t*)workspace;
+  mla::DecodeArgs a{};
+  a.q = q;
+  a.q_fp32 = (q_dtype == MLA_FP32);
+  a.cache = (const uint8_t*)kv_cache;
+  a.page_stride = page_stride_bytes;
+  a.cache_bytes = cache_bytes;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.B = B;
+  a.q_len = q_len;
+  a.H = H;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.n_split = l.S;
+  a.split_rows = 0;                             // each group's union is split evenly in the kernel
+  a.head_begin = 0;
+  a.n_hg = H / 16;
+  a.total_items = l.groups * a.n_hg * l.S;
+  a.items_per_xcd = (a.total_items + 7) / 8;
+  a.out = out;
+  a.lse = lse;
+  a.u_pos = (const int32_t*)ws;
+  a.u_mask = ws + l.mask;
+  a.u_count = (const int32_t*)(ws + l.count);
+  a.u_stride = l.stride;
+  a.groups_per_req = (q_len + 3) / 4;
+  const int64_t T = (int64_t)B * q_len;
+  if (l.S > 1) {
+    a.ws_o = (_Float16*)(ws + l.part);
+    a.ws_lse = (float*)(a.ws_o + T * l.S * H * MLA_LATENT_DIM);
+  }
+  hipError_t e = mla::launch_union(topk_idx, topk, B, q_len, max_pages * MLA_PAGE_ROWS, (int32_t*)ws,
+                                   ws + l.mask, (int32_t*)(ws + l.count), l.stride, stream);
+  if (e != hipSuccess) return hip_status(e, "union kernel launch");
+  if (g_timing_start) {                       // the timing hook brackets the decode kernel only
+    e = hipEventRecord(g_timing_start, stream);
+    if (e != hipSuccess) return hip_status(e, "timing start event");
+  }
+  e = mla::launch_decode_shared(a, stream);
+  if (e != hipSuccess) return hip_status(e, "shared decode kernel launch");
+  if (g_timing_stop) {
+    e = hipEventRecord(g_timing_stop, stream);
+    if (e != hipSuccess) return hip_status(e, "timing stop event");
+  }
+  if (l.S > 1) {
+    e = mla::launch_combine((int32_t)T, H, l.S, a.ws_o, a.ws_lse, out, lse, stream);
+    if (e != hipSuccess) return hip_status(e, "combine kernel launch");
+  }
+  return hip_status(hipSuccess, "");
 }
 
 mla_status mla_fp8_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_cache,

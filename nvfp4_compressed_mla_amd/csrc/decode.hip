@@ -151,8 +151,13 @@ constexpr int kProducers = 8;                                 // producer waves 
 // FP8 selects 576-byte FP8 rows (the baseline format): they need no group scales, so the
 // producer waves load their bytes straight into registers two tiles ahead and convert them,
 // and the math waves issue no gathers.
-template <int NH, bool DENSE, bool FP8>
+// SH (shared rows, NVFP4 sparse with NH = 4 only): the workgroup serves 16 heads of each of up
+// to 4 consecutive query tokens of one request over the union of their lists (a.u_pos), so a
+// row that several of them selected is gathered and decoded once; head block u belongs to token
+// 4g+u and its softmax masks the rows token 4g+u did not select (a.u_mask).
+template <int NH, bool DENSE, bool FP8, bool SH = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
+  static_assert(!SH || (NH == 4 && !DENSE && !FP8), "shared rows: NVFP4 sparse, 4 tokens");
   constexpr int RB = FP8 ? kFp8RowBytes : kRowBytes;     // bytes per cache row
   __shared__ __attribute__((aligned(16))) uint8_t raw[FP8 ? 1 : kRawSlots][FP8 ? 16 : kRawTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t dec[kDecSlots][kDecTileBytes];
@@ -160,6 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   __shared__ __attribute__((aligned(16))) float alpha_s[2][NH * 16];
   __shared__ __attribute__((aligned(16))) int32_t flag_s[2][4];
   __shared__ uint32_t rowoff[DENSE ? kMaxDensePages : kMaxSplitRows];
+  __shared__ __attribute__((aligned(4))) uint8_t rowmask[SH ? kMaxSplitRows : 4];   // SH: token bits
   __shared__ int32_t cnt_s[4][kProducers];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -172,20 +178,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   if (item >= a.total_items) return;
   const int split = item % a.n_split;
   const int rest = item / a.n_split;
-  const int head0 = a.head_begin + (rest % a.n_hg) * 16 * NH;
-  const int tok = rest / a.n_hg;
-  const int b = tok / a.q_len, t = tok % a.q_len;
+  // SH: item = (group of 4 tokens, 16-head block, split); otherwise (token, head group, split)
+  const int head0 = SH ? 16 * (rest % a.n_hg) : a.head_begin + (rest % a.n_hg) * 16 * NH;
+  const int grp = rest / a.n_hg;                         // SH: group index
+  const int tok = SH ? 0 : rest / a.n_hg;
+  const int b = SH ? grp / a.groups_per_req : tok / a.q_len;
+  const int t = SH ? 4 * (grp % a.groups_per_req) : tok % a.q_len;   // SH: the group's first token
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  // token, validity and global 16-head block of the workgroup's head block hb
+  auto hb_tok = [&](int hb) -> int64_t { return SH ? (int64_t)b * a.q_len + t + hb : tok; };
+  auto hb_valid = [&](int hb) -> bool { return !SH || t + hb < a.q_len; };
+  auto hb_global = [&](int hb) -> int { return SH ? (head0 >> 4) : (head0 >> 4) + hb; };
 
   // ---- queries of head block w (math waves) -------------------------------------------------
-  const bool qk_wave = math && w < NH;
+  const bool qk_wave = math && w < NH && hb_valid(w);
   // QK lane block kg carries 8-dim group kdg of each 32-dim chunk (groups 0, 2, 1, 3): the
   // decoded-tile slots of odd groups are XOR-swizzled for the transposing V reads, and with this
   // order lanes 0-31 read unswizzled slots and lanes 32-63 swizzled ones, which keeps the QK
   // fragment reads free of LDS bank conflicts (with kdg = kg every such read was 2-way). The
   // queries follow the same order, so the contraction is unchanged.
   const int kdg = ((kg & 1) << 1) | (kg >> 1);
-  const int64_t qrow = ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kdg;
+  const int64_t qrow = SH ? (hb_tok(qk_wave ? w : 0) * a.H + head0 + l16) * kQkDim + 8 * kdg
+                          : ((int64_t)tok * a.H + head0 + 16 * (qk_wave ? w : 0) + l16) * kQkDim + 8 * kdg;
   half8v qf[kChunks];                         // queries as 18 FP16 fragments (math waves)
   // Loaded after the index compaction (their traffic would otherwise slow its dependent loads
   // down), while the producers' first gathers are in flight; converted to FP16 (softmax_scale *
@@ -231,10 +245,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // Compact the valid entries of [e0, e0 + cnt) into rowoff (16-byte units), in list order:
     // 4 rounds of 512 entries (all index loads first, then all block-table loads), ballot +
     // mbcnt inside a wave, per-wave counts through LDS.
-    const int e0 = split * a.split_rows;
-    const int cnt = max(0, min(a.topk, e0 + a.split_rows) - e0);
     if (!math) {
+      // SH: the group's union is the concatenation of its parts (pre[p] = entries before part
+      // p); it is split evenly (whole tiles) across the splits
+      int pre[kUnionParts + 1];
+      int n_list = a.topk;
+      if constexpr (SH) {
+        pre[0] = 0;
+#pragma unroll
+        for (int p = 0; p < kUnionParts; ++p) pre[p + 1] = pre[p] + a.u_count[grp * kUnionParts + p];
+        n_list = pre[kUnionParts];
+      }
+      const int chunk = SH ? (((n_list + a.n_split - 1) / a.n_split + kTileRows - 1) / kTileRows) * kTileRows
+                           : a.split_rows;
+      const int e0 = split * chunk;
+      const int cnt = max(0, min(n_list, e0 + chunk) - e0);
       const int32_t* idx = a.topk_idx + (int64_t)tok * a.topk + e0;
+      // SH: union entry e of the group -> its place in the parts' arrays
+      auto u_at = [&](int e) -> int64_t {
+        int p = 0;
+#pragma unroll
+        for (int k = 1; k < kUnionParts; ++k) p += (pre[k] <= e) ? 1 : 0;
+        return ((int64_t)grp * kUnionParts + p) * a.u_stride + (e - pre[p]);
+      };
+      uint32_t mk[4] = {0u, 0u, 0u, 0u};      // SH: token masks of the entries
       // Branch-free loads (clamped addresses, results selected afterwards) so that all index
       // loads are in flight together, then all block-table loads.
       int jv[4] = {-1, -1, -1, -1}, pg[4] = {-1, -1, -1, -1};
@@ -242,8 +276,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = r * 512 + ptid;
-          const int v = idx[min(e, cnt - 1)];
-          jv[r] = (e < cnt) ? v : -1;
+          if constexpr (SH) {
+            const int64_t ue = u_at(e0 + min(e, cnt - 1));
+            jv[r] = (e < cnt) ? a.u_pos[ue] : -1;
+            mk[r] = a.u_mask[ue];
+          } else {
+            const int v = idx[min(e, cnt - 1)];
+            jv[r] = (e < cnt) ? v : -1;
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -278,7 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         const uint64_t mask = __ballot(ok);
         const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (ok) rowoff[n_rows + before + below] = (uint32_t)jv[r];
+        if (ok) {
+          rowoff[n_rows + before + below] = (uint32_t)jv[r];
+          if constexpr (SH) rowmask[n_rows + before + below] = (uint8_t)mk[r];
+        }
         n_rows += total;
       }
     } else {
@@ -325,16 +368,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const bool final_out = (a.n_split == 1);
 #pragma unroll
       for (int hb = 0; hb < NH; ++hb) {
-        const int hbg = (head0 >> 4) + hb;
+        if (!hb_valid(hb)) continue;
+        const int hbg = hb_global(hb);
+        const int64_t otok = hb_tok(hb);
         if (final_out) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float* dst = a.out + ((int64_t)tok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
+            float* dst = a.out + (otok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
 #pragma unroll
             for (int n = 0; n < 4; ++n) dst[16 * n] = 0.0f;
           }
         } else {
-          _Float16* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+          _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
 #pragma unroll
           for (int n = 0; n < 4; ++n) *(uint2v*)(dst + 256 * n) = uint2v{0u, 0u};
         }
@@ -343,9 +388,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int e = 0; e < 4; ++e) {
             const int head = 16 * hbg + 4 * kg + e;
             if (final_out) {
-              if (a.lse) a.lse[(int64_t)tok * a.H + head] = -INFINITY;
+              if (a.lse) a.lse[otok * a.H + head] = -INFINITY;
             } else {
-              a.ws_lse[((int64_t)tok * a.n_split + split) * a.H + head] = -INFINITY;
+              a.ws_lse[(otok * a.n_split + split) * a.H + head] = -INFINITY;
             }
           }
         }
@@ -447,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           if constexpr (!FP8) tile_offsets(i + 4, next_o16);   // LDS latency hides behind the softmax
           float sv[8];
           float mx = -INFINITY;
-          const bool full = (i + 1) * kTileRows <= n_rows && dense_ok;
+          const bool full = !SH && (i + 1) * kTileRows <= n_rows && dense_ok;
           if (full) {                                        // full tile: no row mask
   #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -462,11 +507,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               const float4v sc = acc[rb][0] + acc[rb][1];
+              // SH: the token bits of rows 16*rb + 4*kg .. +3 (one byte each)
+              const uint32_t mw = SH ? *(const uint32_t*)&rowmask[i * kTileRows + 16 * rb + 4 * kg] : 0u;
   #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int row = i * kTileRows + 16 * rb + 4 * kg + e;
                 bool ok = row < n_rows;
                 if constexpr (DENSE) ok = ok && (dense_ok || row_o16(row) != kInvalid);
+                if constexpr (SH) ok = ok && ((mw >> (8 * e + w)) & 1u);
                 sv[4 * rb + e] = ok ? sc[e] * a.scale_log2 : -INFINITY;
                 mx = fmaxf(mx, sv[4 * rb + e]);
               }
@@ -683,16 +731,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     const bool final_out = (a.n_split == 1);
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
+      if (!hb_valid(hb)) continue;
       const float4v mm = *(const float4v*)&fin_m[16 * hb + 4 * kg];
       const float4v ll = *(const float4v*)&fin_l[16 * hb + 4 * kg];
       float4v inv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) inv[e] = ll[e] > 0.0f ? 1.0f / ll[e] : 0.0f;
-      const int hbg = (head0 >> 4) + hb;                  // global 16-head block
+      const int hbg = hb_global(hb);                      // global 16-head block
+      const int64_t otok = hb_tok(hb);
       if (final_out) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float* dst = a.out + ((int64_t)tok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
+          float* dst = a.out + (otok * a.H + 16 * hbg + 4 * kg + e) * kLatent + 64 * pw + l16;
 #pragma unroll
           for (int n = 0; n < 4; ++n) dst[16 * n] = o[hb][n][e] * inv[e];
         }
@@ -703,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         // write-back, which shortens this kernel by more than the combine, whose single round of
         // loads then reads them from the memory-side cache, loses. With more splits the combine
         // reads in several rounds and the partials are better kept in the L2.
-        _Float16* dst = a.ws_o + ((((int64_t)tok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+        _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
         const bool stream = a.n_split <= kStreamPartialSplits;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
@@ -722,9 +772,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           const float lse_v = ll[e] > 0.0f
               ? (mm[e] + __builtin_amdgcn_logf(ll[e])) * 0.69314718055994530942f : -INFINITY;
           if (final_out) {
-            if (a.lse) a.lse[(int64_t)tok * a.H + head] = lse_v;
+            if (a.lse) a.lse[otok * a.H + head] = lse_v;
           } else {
-            a.ws_lse[((int64_t)tok * a.n_split + split) * a.H + head] = lse_v;
+            a.ws_lse[(otok * a.n_split + split) * a.H + head] = lse_v;
           }
         }
       }
@@ -846,6 +896,12 @@ hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipS
   }
 #undef MLA_CASES
 #undef MLA_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<4, false, false, true>), dim3((unsigned)a.items_per_xcd * 8),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,14 @@ struct DecodeArgs {
   float* lse;               // [T, H] or null (n_split == 1)
   _Float16* ws_o;           // [T, n_split, H/16, 32, 64, 4] FP16 partial outputs (n_split > 1)
   float* ws_lse;            // [T, n_split, H] partial log-sum-exp (natural log)
+  // Shared-row mode (the rows selected by a group of up to 4 consecutive query tokens of one
+  // request, deduplicated): workgroup = (group, 16-head block, split), head block u of the
+  // workgroup = token 4g+u of the group.
+  const int32_t* u_pos;     // [n_groups, kUnionParts, u_stride] union positions, ascending
+  const uint8_t* u_mask;    // same layout; bit u: token 4g+u selected the position
+  const int32_t* u_count;   // [n_groups, kUnionParts] entries of each part
+  int32_t u_stride;
+  int32_t groups_per_req;   // ceil(q_len / 4)
 };
 
 constexpr int kMaxSplitRows = 2048;   // sparse rows per split held in LDS
@@ -48,6 +56,21 @@ hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_
 // nh = heads per workgroup / 16 (1..4); dense selects implicit positions; fp8 selects 576-byte
 // FP8 rows instead of 352-byte NVFP4 rows.
 hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream);
+
+// Shared-row decode (NVFP4 rows, 4 tokens x 16 heads per workgroup) over the unions built by
+// launch_union.
+hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream);
+
+// Union of the index lists of each group of up to 4 consecutive query tokens of a request:
+// ascending distinct positions in [0, n_pos) and their 4-bit token masks, in kUnionParts parts
+// (equal position ranges) of u_stride entries each, u_count[group * kUnionParts + part] entries
+// used. n_pos <= kUnionMaxPos, topk <= kUnionMaxTopk.
+constexpr int kUnionMaxPos = 1 << 20;
+constexpr int kUnionParts = 16;
+constexpr int kUnionMaxTopk = 2048;
+hipError_t launch_union(const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                        int32_t n_pos, int32_t* u_pos, uint8_t* u_mask, int32_t* u_count,
+                        int32_t u_stride, hipStream_t stream);
 
 hipError_t launch_fp8_append(const void* latent, int64_t latent_stride, const void* rope,
                              int64_t rope_stride, const int64_t* slots, int64_t n_rows, void* cache,
