@@ -600,6 +600,38 @@ def run_config(wk, steps, warmup, prof_launches):
     }
 
 
+def counter_target(name, dev, launches=4):
+    """Eager launches of one workload and nothing else, for rocprofv3 counter passes."""
+    import torch
+    from nvfp4_compressed_mla_amd import workloads as wl
+    if name == "mixed_append":
+        mx = wl.named_workload("mixed")
+        mw = SparseWorkload("mixed", mx.B, 15, 64, [c + 6144 for c in mx.ctx], 2048, 6144, 1, 1004,
+                            dev, q_lens=mx.q_lens)
+        torch.cuda.synchronize()
+        log("[bench] counter target: mixed-step append (393,216 rows)")
+        for _ in range(launches):
+            mw.append()
+    else:
+        for f in (0.0, 0.9):
+            w64 = SparseWorkload("mtp_ov", 16, 15, 64, [149504] * 16, 2048, 0, 1, 1005, dev, overlap=f)
+            log(f"[bench] counter target: MTP overlap {f}, 64 heads, per-token decode")
+            for _ in range(launches):
+                w64.decode(0)
+            torch.cuda.synchronize()
+            del w64
+            w16 = SparseWorkload("mtp_ov16", 16, 15, 16, [149504] * 16, 2048, 0, 1, 1007, dev, overlap=f)
+            w16.use_shared_rows()
+            log(f"[bench] counter target: MTP overlap {f}, 16 heads, shared rows")
+            for _ in range(launches):
+                w16.decode(0)
+            torch.cuda.synchronize()
+            del w16
+            torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_target": name, "launches": launches}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -615,6 +647,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--counter-target", choices=("mixed_append", "mtp_overlap"),
+                    help="only run a few eager launches of one workload (a target for counter "
+                         "passes): the mixed step's 393,216-row append, or the MTP shape under the "
+                         "overlap model (f = 0 and 0.9; per-token at 64 heads, shared rows at 16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -642,6 +678,10 @@ def main():
 
     import nvfp4_compressed_mla_amd as m
     m.load_library()                         # raises if the HIP library was not built
+
+    if args.counter_target:
+        counter_target(args.counter_target, dev)
+        return
 
     log("[bench] building batched workload (B=32, H=64, 143,360-token caches, top-k 2048)")
     t_setup = time.perf_counter()
