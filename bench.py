@@ -34,6 +34,7 @@ FP8_PAGE = 64 * 576
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batched_counters.txt")
+SPIN_CYCLES = 2_000_000          # GPU spin before a timed region (about a millisecond)
 KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_compressed_mla_amd", "csrc", f)
                   for f in ("decode.hip", "nvfp4_device.h")]
 
@@ -255,7 +256,8 @@ def _graph_plan(rot, n, tail_at_end):
 
 
 def time_steps(fn, rot, steps, warmup, stats=None):
-    """Replay captured graphs for `warmup` then exactly `steps` steps; returns wall ms per step.
+    """Replay captured graphs for `warmup` then exactly `steps` steps; returns ms per step, timed
+    with HIP events on the replay stream around the whole timed region.
 
     Every replay is a whole multi-step graph (a full pass over the `rot` rotations, or one graph
     of the remaining steps), so the per-step figure does not depend on how `steps` divides by
@@ -277,13 +279,19 @@ def time_steps(fn, rot, steps, warmup, stats=None):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in time_plan]
-    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # A GPU spin ahead of the timed replays: the host queues them while it runs, so that no
+    # replay waits for its own submission (a single 20-step graph would otherwise carry the
+    # whole submission latency, a 48-step one a smaller share of it). The timed region is the
+    # stream's own: from the event after the spin to the event after the last replay.
+    torch.cuda._sleep(SPIN_CYCLES)
+    start.record()
     for key, (a, b) in zip(time_plan, evs):
         a.record()
         graphs[key].replay()
         b.record()
+    end.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     if stats is not None:
         per = sorted(a.elapsed_time(b) * 1e3 / key[0] for key, (a, b) in zip(time_plan, evs))
 
@@ -292,7 +300,7 @@ def time_steps(fn, rot, steps, warmup, stats=None):
         stats.update({"median_us": round(pct(0.5), 3), "p10_us": round(pct(0.1), 3),
                       "p90_us": round(pct(0.9), 3), "replays": len(per),
                       "steps_per_replay": sorted({k[0] for k in time_plan})})
-    return (t1 - t0) * 1e3 / steps
+    return start.elapsed_time(end) / steps
 
 
 def time_decode_kernel(wk, launches):
@@ -723,6 +731,8 @@ def main():
                                "block tables",
                    "global_batch": 32, "seq_len": 143360, "topk": 2048, "heads": 64,
                    "rotations": wk.rot, "splits": wk.splits},
+        "step_timing": "HIP events on the replay stream around exactly `steps` graph-replayed steps, "
+                       "after a GPU spin that lets the host queue the replays ahead of the GPU",
         "step_replays_us": step_stats,
         "us_per_launch": round(ms_dec * 1e3, 2),
         "launch_replays_us": dec_stats,
