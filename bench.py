@@ -35,6 +35,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batched_counters.txt")
 SPIN_CYCLES = 2_000_000          # GPU spin before a timed region (about a millisecond)
+HEAT_MS = 30.0                   # GPU work replayed before the warmup of every timed region
 KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_compressed_mla_amd", "csrc", f)
                   for f in ("decode.hip", "nvfp4_device.h")]
 
@@ -270,10 +271,20 @@ def time_steps(fn, rot, steps, warmup, stats=None):
     time_plan = _graph_plan(rot, steps, False)
     for key in set(warm_plan + time_plan):
         graphs[key] = capture(fn, key[0], key[1])
-    # the first replay of a captured graph carries one-time costs: pay them for every timed graph
-    # before the warmup (which then moves the infinity cache away from the timed rotations)
-    for key in set(time_plan):
-        graphs[key].replay()
+    # The first replay of a captured graph carries one-time costs: pay them for every timed graph
+    # before the warmup (which then moves the infinity cache away from the timed rotations).
+    # The timed graphs are replayed until at least HEAT_MS of GPU work has run, so that the GPU
+    # enters the warmup in the same state whatever the step counts (a 20-step timing after a
+    # 5-step warmup otherwise measured a GPU still settling from the setup).
+    heat = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+    heat[0].record()
+    while True:
+        for key in set(time_plan):
+            graphs[key].replay()
+        heat[1].record()
+        torch.cuda.synchronize()
+        if heat[0].elapsed_time(heat[1]) >= HEAT_MS or not time_plan:
+            break
     for key in warm_plan:
         graphs[key].replay()
     torch.cuda.synchronize()
