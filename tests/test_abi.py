@@ -240,3 +240,51 @@ def test_dense_one_wave_split_helper(lib):
             assert T * groups * ns(P, st) <= 256
     assert f(0, 64, 10) == 4096 and f(4, 8, 10) == 4096
 
+
+
+def test_indexer_entry_point_rejects(lib):
+    f = lib.mla_indexer_scores
+    args = dict(q=FAKE, w=FAKE, c=FAKE, stride=8448, cb=8448 * 4, bt=FAKE, mp=4, sl=FAKE, B=1, ql=2,
+                n=256, s=FAKE)
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return f(a["q"], a["w"], a["c"], a["stride"], a["cb"], a["bt"], a["mp"], a["sl"], a["B"],
+                 a["ql"], a["n"], a["s"], None)
+    for k in ("q", "w", "c", "bt", "sl", "s"):
+        assert call(**{k: None}) == INVALID, k
+    assert call(stride=8448 - 16) == INVALID          # smaller than a page
+    assert call(stride=8448 + 8) == INVALID           # not a multiple of 16
+    assert call(c=ctypes.c_void_p(0x10008)) == INVALID
+    assert call(q=ctypes.c_void_p(0x10004)) == INVALID
+    assert call(w=ctypes.c_void_p(0x10004)) == INVALID
+    assert call(cb=100) == INVALID
+    assert call(B=0) == INVALID and call(B=65536) == INVALID and call(ql=0) == INVALID
+    assert call(mp=0) == INVALID
+    assert call(n=0) == INVALID and call(n=(1 << 20) + 1) == INVALID
+
+
+def test_shared_decode_entry_points(lib):
+    f = lib.mla_sparse_decode_shared
+    # 16 requests x 15 tokens -> 64 groups of 4; 4 splits at top-k 2048 (8,192-entry unions in
+    # lists of at most 2,048 rows), 16 parts of 8,192 entries per group
+    assert lib.mla_shared_decode_num_splits(16, 15, 16, 2048) == 4
+    assert lib.mla_shared_decode_num_splits(1, 4, 16, 64) == 16
+    n = 64 * 16 * 8192
+    r256 = lambda b: (b + 255) // 256 * 256
+    expect = r256(n * 4) + r256(n) + r256(64 * 16 * 4) + r256(240 * 4 * 16 * (512 * 2 + 4))
+    assert lib.mla_shared_decode_workspace_size(16, 15, 16, 2048) == expect
+    assert lib.mla_shared_decode_workspace_size(0, 15, 16, 2048) == 0
+    args = dict(q=FAKE, qd=0, c=FAKE, stride=22528, cb=22528 * 4, bt=FAKE, mp=4, idx=FAKE, k=256,
+                B=1, ql=4, H=16, sc=0.04, out=FAKE, lse=None, ws=FAKE, wb=1 << 30)
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return f(a["q"], a["qd"], a["c"], a["stride"], a["cb"], a["bt"], a["mp"], a["idx"], a["k"],
+                 a["B"], a["ql"], a["H"], a["sc"], a["out"], a["lse"], a["ws"], a["wb"], None)
+    assert call(idx=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(k=0) == UNSUPPORTED and call(k=2049) == UNSUPPORTED
+    assert call(H=24) == UNSUPPORTED
+    assert call(mp=16385) == UNSUPPORTED              # more than 2^20 positions
+    assert call(ws=None) == WORKSPACE
+    assert call(wb=1024) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE
