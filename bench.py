@@ -130,8 +130,20 @@ class SparseWorkload:
         self.splits = m.mla_shared_decode_num_splits(self.B, self.q_len, self.H, self.topk)
         self.fmt = "shared"
 
+    def use_fused_append(self):
+        """From now on a step is one fused append + decode call (the same cache bytes and result
+        as the append followed by the decode); needs one appended row per query token."""
+        assert self.fmt == "nvfp4" and self.append_rows == self.q_len
+        self.fmt = "fused"
+
     def decode(self, r):
         import nvfp4_compressed_mla_amd as m
+        if self.fmt == "fused":
+            m.mla_sparse_decode_append(self.q[r], self.cache, self.page, self.block_table, self.idx[r],
+                                       1.0 / math.sqrt(576.0), self.new_lat, self.new_rope,
+                                       self.new_slots, out=self.out, lse=self.lse,
+                                       num_splits=self.splits, workspace=self.ws)
+            return
         if self.fmt == "shared":
             m.mla_sparse_decode_shared(self.q[r], self.cache, self.page, self.block_table, self.idx[r],
                                        1.0 / math.sqrt(576.0), out=self.out, lse=self.lse,
@@ -144,7 +156,7 @@ class SparseWorkload:
 
     def append(self):
         import nvfp4_compressed_mla_amd as m
-        if self.append_rows:
+        if self.append_rows and self.fmt != "fused":      # the fused call appends itself
             fn = m.mla_fp8_append if self.fmt == "fp8" else m.mla_nvfp4_quantize_append
             fn(self.new_lat, self.new_rope, self.new_slots, self.cache, self.page)
 
@@ -152,11 +164,13 @@ class SparseWorkload:
         self.append()
         self.decode(r)
 
-    # algorithmic bytes / flops of the fused decode kernel for rotation r
+    # algorithmic bytes / flops of the fused decode kernel for rotation r (with the fused append:
+    # plus the appended rows' bf16 input, 352-byte output and slot)
     def kernel_bytes(self, r):
         T = self.B * self.q_len
         qb = 4 if self.q_dtype == "fp32" else 2
-        return self.valid_pairs[r] * (self.row_bytes + 4 + 4) + T * self.H * 576 * qb
+        app = self.append_rows * self.B * (1152 + 352 + 8) if self.fmt == "fused" else 0
+        return self.valid_pairs[r] * (self.row_bytes + 4 + 4) + T * self.H * 576 * qb + app
 
     def launch_bytes(self, r):
         """The whole decode launch (fused kernel + combine): the kernel's bytes plus the fp32
@@ -709,12 +723,18 @@ def main():
                         keep_latent=not args.no_cpu_baseline)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; splits={wk.splits}")
 
+    # the step as three launches (append, decode, merge), then the headline: the append fused
+    # into the decode kernel (two launches)
+    sep_stats = {}
+    ms_sep = time_steps(wk.step, wk.rot, max(args.steps // 2, wk.rot), args.warmup, sep_stats)
+    log(f"[bench] append + decode step {ms_sep * 1e3:.2f} us (replays: {sep_stats})")
+    wk.use_fused_append()
     step_stats, dec_stats = {}, {}
     ms_step = time_steps(wk.step, wk.rot, args.steps, args.warmup, step_stats)
-    log(f"[bench] step {ms_step * 1e3:.2f} us (replays: {step_stats})")
+    log(f"[bench] fused step {ms_step * 1e3:.2f} us (replays: {step_stats})")
     ms_dec = time_steps(wk.decode, wk.rot, max(args.steps // 2, wk.rot), args.warmup, dec_stats)
     kavg, kd = time_decode_kernel(wk, args.prof_launches)
-    log(f"[bench] decode launch {ms_dec * 1e3:.2f} us, fused kernel {kavg * 1e3:.2f} us")
+    log(f"[bench] fused launch {ms_dec * 1e3:.2f} us, fused kernel {kavg * 1e3:.2f} us")
 
     gathered = sum(wk.gathered_bytes(r) for r in range(wk.rot)) / wk.rot
     kbytes = sum(wk.kernel_bytes(r) for r in range(wk.rot)) / wk.rot
@@ -744,14 +764,19 @@ def main():
                    "rotations": wk.rot, "splits": wk.splits},
         "step_timing": "HIP events on the replay stream around exactly `steps` graph-replayed steps, "
                        "after a GPU spin that lets the host queue the replays ahead of the GPU",
+        "step": "one mla_sparse_decode_append call (the 32 new rows quantize-appended inside the "
+                "decode kernel) + the split merge",
         "step_replays_us": step_stats,
+        "step_append_then_decode_us": round(ms_sep * 1e3, 3),
+        "step_append_then_decode_replays_us": sep_stats,
         "us_per_launch": round(ms_dec * 1e3, 2),
         "launch_replays_us": dec_stats,
         "gathered_GBps_per_launch": round(gathered / (ms_dec * 1e-3) / 1e9, 1),
         "gathered_pct_of_peak": round(100 * gathered / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"decode_kernel<{head_group_blocks(64)},false,false> (fused gather/decode/QK/softmax/PV)",
+            "kernel": f"decode_kernel<{head_group_blocks(64)},false,false,false,true> (fused append/gather/"
+                      "decode/QK/softmax/PV)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -768,8 +793,8 @@ def main():
         },
         "roofline_launch": {
             "bound": "hbm",
-            "what": "whole decode launch (fused kernel + split combine), graph-replayed; bytes "
-                    "include the fp32 output and lse",
+            "what": "whole launch (fused append + decode kernel, split combine), graph-replayed; "
+                    "bytes include the fp32 output and lse",
             "achieved": round(lbytes / (ms_dec * 1e-3) / 1e9, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -129,6 +129,33 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype,
                              int32_t num_splits, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Quantize-append fused into the sparse decode (page section "Making room for low-latency
+ * decode": the new latent rows are stored as NVFP4; section "Native NVFP4 sparse MLA decode
+ * kernel": the decode reads the selected rows, which in a decode step include the rows the step
+ * itself appends). One call does what mla_nvfp4_quantize_append(latent, rope, slot_mapping,
+ * B*q_len) followed by mla_sparse_decode(...) does, in one decode launch (plus the split merge):
+ *   latent, rope, latent_row_stride, rope_row_stride   as mla_nvfp4_quantize_append, with
+ *              B*q_len rows: row b*q_len + t is the new row of query token t of request b;
+ *   slot_mapping int64 [B*q_len] its physical slot; -1 = not appended;
+ *   kv_cache   written: each appended row's 352 bytes, as mla_nvfp4_quantize_append writes them
+ *              (the same encoder); every other argument, the workspace included, as
+ *              mla_sparse_decode.
+ * Every decode workgroup of request b encodes that request's q_len new rows and stores them to
+ * their slots before it gathers any row, so whatever it reads of those rows is the new bytes
+ * (other workgroups store the same bytes at the same time).
+ * Requirements beyond mla_sparse_decode's: q_len <= 16; the slots of one call are distinct; no
+ * request's list resolves to a row appended for another request in the same call (such an entry
+ * may read the row before or after the append). */
+mla_status mla_sparse_decode_append(const void* q, mla_dtype q_dtype, void* kv_cache,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                                    int32_t H, float softmax_scale, int32_t num_splits,
+                                    const void* latent, int64_t latent_row_stride,
+                                    const void* rope, int64_t rope_row_stride,
+                                    const int64_t* slot_mapping, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Sparse decode with rows shared across query tokens (page section "Native NVFP4 sparse MLA
  * decode kernel": a launch carries several query tokens of a request, 15 in the page's figure).
  * Same arguments and result as mla_sparse_decode; the work is split differently: the lists of

@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     mla_shared_decode_num_splits,
     mla_shared_decode_workspace_size,
     mla_sparse_decode,
+    mla_sparse_decode_append,
     mla_sparse_decode_shared,
     mla_sparse_decode_num_splits,
     mla_staged_sparse_decode,

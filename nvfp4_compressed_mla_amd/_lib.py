@@ -29,6 +29,7 @@ EXPORTED = [
     "mla_dense_decode_num_splits",
     "mla_dense_decode_split_tokens",
     "mla_sparse_decode",
+    "mla_sparse_decode_append",
     "mla_shared_decode_workspace_size",
     "mla_shared_decode_num_splits",
     "mla_sparse_decode_shared",
@@ -96,6 +97,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_sparse_decode.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32, i32,
                                       i32, f32, i32, vp, vp, vp, sz, vp]
     lib.mla_sparse_decode.restype = ctypes.c_int
+    lib.mla_sparse_decode_append.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i32, vp, i32, i32,
+                                             i32, i32, f32, i32, vp, i64, vp, i64, vp, vp, vp, vp,
+                                             sz, vp]
+    lib.mla_sparse_decode_append.restype = ctypes.c_int
     lib.mla_shared_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.mla_shared_decode_workspace_size.restype = sz
     lib.mla_shared_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -285,6 +290,46 @@ def mla_sparse_decode(q, kv_cache, page_stride_bytes, block_table, topk_idx, sof
     """
     return _sparse("mla_sparse_decode", q, kv_cache, page_stride_bytes, block_table, topk_idx,
                    softmax_scale, out, lse, num_splits, workspace, want_lse, stream)
+
+
+def mla_sparse_decode_append(q, kv_cache, page_stride_bytes, block_table, topk_idx, softmax_scale,
+                             latent, rope, slot_mapping, out=None, lse=None, num_splits: int = 0,
+                             workspace=None, want_lse=True, stream=None):
+    """Quantize-append of one new row per query token (``latent`` bf16 [B*q_len, 512], ``rope``
+    bf16 [B*q_len, 64], ``slot_mapping`` int64 [B*q_len]) fused into the sparse decode: the same
+    cache bytes and result as :func:`mla_nvfp4_quantize_append` then :func:`mla_sparse_decode`.
+    Returns (out, lse)."""
+    torch = _torch()
+    _require(q, "q")
+    _require(kv_cache, "kv_cache", torch.uint8)
+    _require(block_table, "block_table", torch.int32)
+    _require(topk_idx, "topk_idx", torch.int32)
+    _require(latent, "latent", torch.bfloat16)
+    _require(rope, "rope", torch.bfloat16)
+    _require(slot_mapping, "slot_mapping", torch.int64)
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, q_len, H, 576]")
+    B, q_len, H, _ = q.shape
+    if topk_idx.dim() != 3 or tuple(topk_idx.shape[:2]) != (B, q_len) or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous int32 [B, q_len, topk]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    if latent.dim() != 2 or tuple(latent.shape) != (B * q_len, 512) or latent.stride(1) != 1:
+        raise ValueError("latent must be [B*q_len, 512] with unit inner stride")
+    if rope.dim() != 2 or tuple(rope.shape) != (B * q_len, 64) or rope.stride(1) != 1:
+        raise ValueError("rope must be [B*q_len, 64] with unit inner stride")
+    if not slot_mapping.is_contiguous() or slot_mapping.numel() != B * q_len:
+        raise ValueError("slot_mapping must be contiguous int64 [B*q_len]")
+    topk = topk_idx.shape[2]
+    splits = num_splits or mla_sparse_decode_num_splits(B * q_len, H, topk, 0)
+    out, lse = _outputs(q, out, lse, want_lse)
+    workspace, ws_bytes = _workspace(workspace, B * q_len, H, splits, q.device)
+    _check(load_library().mla_sparse_decode_append(
+        _ptr(q), _q_dtype(q), _ptr(kv_cache), int(page_stride_bytes), kv_cache.numel(),
+        _ptr(block_table), block_table.shape[1], _ptr(topk_idx), topk, B, q_len, H,
+        float(softmax_scale), splits, _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+        _ptr(slot_mapping), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
 
 
 def mla_shared_decode_workspace_size(B: int, q_len: int, H: int, topk: int) -> int:

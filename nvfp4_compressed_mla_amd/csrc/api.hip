@@ -334,18 +334,37 @@ int32_t mla_dense_decode_num_splits(int32_t max_pages, int32_t split_tokens) {
 
 namespace {
 
+// The new rows of a fused append + sparse decode (mla_sparse_decode_append).
+struct AppendIn {
+  const void* latent;
+  int64_t latent_stride;
+  const void* rope;
+  int64_t rope_stride;
+  const int64_t* slots;
+  void* cache;
+};
+
 mla_status sparse_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const void* kv_cache,
                               int64_t page_stride_bytes, int64_t cache_bytes,
                               const int32_t* block_table, int32_t max_pages,
                               const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
                               int32_t H, float softmax_scale, int32_t num_splits, float* out,
                               float* lse, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+                              hipStream_t stream, const AppendIn* ap = nullptr) {
   mla_status st = check_decode_common(q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
                                       block_table, max_pages, B, q_len, H, softmax_scale,
                                       num_splits, out, lse, workspace, workspace_bytes,
                                       fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
   if (st != MLA_OK) return st;
+  if (ap) {
+    if (q_len > mla::kApMaxRows) return fail(MLA_ERR_UNSUPPORTED, "fused append: q_len %d > %d", q_len, mla::kApMaxRows);
+    if (!ap->latent || !ap->rope || !ap->slots) return fail(MLA_ERR_INVALID_ARG, "null latent / rope / slot_mapping");
+    if (!aligned(ap->latent, 16) || ap->latent_stride < MLA_LATENT_DIM || ap->latent_stride % 8 != 0)
+      return fail(MLA_ERR_INVALID_ARG, "latent must be 16-byte aligned with a row stride >= 512 and a multiple of 8");
+    if (!aligned(ap->rope, 2) || ap->rope_stride < MLA_ROPE_DIM)
+      return fail(MLA_ERR_INVALID_ARG, "rope must be 2-byte aligned with a row stride >= 64");
+    if (!aligned(ap->slots, 8)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  }
   if (!topk_idx) return fail(MLA_ERR_INVALID_ARG, "topk_idx is null");
   if (topk < 1 || topk > MLA_MAX_TOPK) return fail(MLA_ERR_UNSUPPORTED, "topk %d outside [1, 2048]", topk);
   if (!aligned(topk_idx, 4) || !aligned(block_table, 4)) return fail(MLA_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
@@ -381,6 +400,19 @@ mla_status sparse_decode_impl(bool fp8, const void* q, mla_dtype q_dtype, const 
     st = mla_check_sparse_indices(hi.data(), B, q_len, topk, hb.data(), max_pages, page_stride_bytes,
                                   cache_bytes, fp8 ? MLA_FP8_ROW_BYTES : MLA_ROW_BYTES);
     if (st != MLA_OK) return st;
+    if (ap) {
+      std::vector<int64_t> hs;
+      if ((st = debug_copy(hs, ap->slots, (size_t)T, stream, "slot_mapping")) != MLA_OK) return st;
+      if ((st = mla_check_slots(hs.data(), T, page_stride_bytes, cache_bytes, MLA_ROW_BYTES)) != MLA_OK) return st;
+    }
+  }
+  if (ap) {
+    a.ap_latent = (const uint16_t*)ap->latent;
+    a.ap_latent_stride = ap->latent_stride;
+    a.ap_rope = (const uint16_t*)ap->rope;
+    a.ap_rope_stride = ap->rope_stride;
+    a.ap_slots = ap->slots;
+    a.ap_cache = (uint8_t*)ap->cache;
   }
   return run_decode(a, H, false, fp8, stream);
 }
@@ -495,6 +527,21 @@ mla_status mla_sparse_decode(const void* q, mla_dtype q_dtype, const void* kv_ca
   return sparse_decode_impl(false, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
                             block_table, max_pages, topk_idx, topk, B, q_len, H, softmax_scale,
                             num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_sparse_decode_append(const void* q, mla_dtype q_dtype, void* kv_cache,
+                                    int64_t page_stride_bytes, int64_t cache_bytes,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* topk_idx, int32_t topk, int32_t B, int32_t q_len,
+                                    int32_t H, float softmax_scale, int32_t num_splits,
+                                    const void* latent, int64_t latent_row_stride,
+                                    const void* rope, int64_t rope_row_stride,
+                                    const int64_t* slot_mapping, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const AppendIn ap{latent, latent_row_stride, rope, rope_row_stride, slot_mapping, kv_cache};
+  return sparse_decode_impl(false, q, q_dtype, kv_cache, page_stride_bytes, cache_bytes,
+                            block_table, max_pages, topk_idx, topk, B, q_len, H, softmax_scale,
+                            num_splits, out, lse, workspace, workspace_bytes, stream, &ap);
 }
 
 size_t mla_shared_decode_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t topk) {

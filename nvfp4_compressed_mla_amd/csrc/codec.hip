@@ -18,14 +18,13 @@
 
 namespace mla {
 
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
-
 // Layout: lane l of a wavefront owns group g = l & 31 (16 latent values) of row 2i + (l >> 5),
 // so the per-group work (amax, scale byte, grid midpoints) is done once per group and each half
 // of the wave encodes one row. A wave takes PAIRS row pairs per iteration and issues all their
 // loads (slots, latent, rope) before encoding the first, which keeps several rows in flight
 // (PAIRS = 2 for large appends; small appends take one pair per wave, for the shortest latency).
-// The kernel is bound by its integer/compare arithmetic more than by its 1,512 bytes per row.
+// The encode is shared with the fused append + decode kernel (nvfp4_encode_lane), so both write
+// the same bytes.
 constexpr int64_t kAppendLargeRows = 65536;   // from here on two row pairs per wave
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
@@ -72,43 +71,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
       // rows past the end, slots of -1 and slots outside the cache are not written
       const bool write = row < n_rows && slot >= 0 && off >= 0 && off + kRowBytes <= cache_bytes;
 
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_bits_to_float(xa[p][i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_bits_to_float(xa[p][i] >> 16);
-        v[8 + 2 * i] = bf16_bits_to_float(xb[p][i] & 0xFFFFu);
-        v[8 + 2 * i + 1] = bf16_bits_to_float(xb[p][i] >> 16);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-      // amax * fl(1/6) rounds to the same E4M3 byte as the exact quotient amax / 6 for every
-      // finite bf16 amax (checked exhaustively on the host), at the cost of one multiply.
-      const uint32_t sbyte = e4m3_encode2_hw(amax * (1.0f / 6.0f), 0.0f) & 0xFFu;
-      const float sc = e4m3_to_float_hw(sbyte);
-      const float rinv = sc > 0.0f ? 1.0f / sc : 0.0f;          // IEEE division, once per group
-      const float bound = 8.0f * fmaxf(sc, 0x1p-20f);
-      const uint32_t c0 = e2m1_encode8_hw(v, sc, rinv, bound);        // elements 0..7
-      const uint32_t c1 = e2m1_encode8_hw(v + 8, sc, rinv, bound);    // elements 8..15
-      const uint32_t rpair = e4m3_encode2_hw(bf16_bits_to_float(ra[p]), bf16_bits_to_float(rb[p]));
-      const uint32_t rba = rpair & 0xFFu, rbb = rpair >> 8;
-
-      // Words of bytes 256..351: scale dword k (groups 4k..4k+3) is built on lane 4k of the
-      // half, rope dword k (elements 4k..4k+3) on lane 4k (k < 8) or 4(k - 8) (k >= 8).
-      const uint32_t sword = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
-                             (__shfl_down(sbyte, 3) << 24);
-      const uint32_t rwa = rba | (__shfl_down(rba, 1) << 8) | (__shfl_down(rba, 2) << 16) |
-                           (__shfl_down(rba, 3) << 24);
-      const uint32_t rwb = rbb | (__shfl_down(rbb, 1) << 8) | (__shfl_down(rbb, 2) << 16) |
-                           (__shfl_down(rbb, 3) << 24);
-      const int src = (lane & 32) | (4 * (lane & 7));
-      const uint32_t w_s = __shfl(sword, src), w_a = __shfl(rwa, src), w_b = __shfl(rwb, src);
+      const Nvfp4LaneOut e = nvfp4_encode_lane(xa[p], xb[p], ra[p], rb[p]);
       if (write) {
         uint8_t* dst = cache + off;
-        *(uint2v*)(dst + 8 * g) = uint2v{c0, c1};                  // bytes 0..255: codes
-        if (g < 24)                                                 // bytes 256..351
-          ((uint32_t*)(dst + kScaleOff))[g] = g < 8 ? w_s : (g < 16 ? w_a : w_b);
+        *(uint2v*)(dst + 8 * g) = uint2v{e.c0, e.c1};              // bytes 0..255: codes
+        if (g < 24) ((uint32_t*)(dst + kScaleOff))[g] = e.tail;     // bytes 256..351
       }
     }
   }

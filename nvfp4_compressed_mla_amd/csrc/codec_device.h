@@ -93,4 +93,55 @@ __device__ __forceinline__ uint32_t e2m1_encode8_hw(const float* x, float s, flo
   return w;
 }
 
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// One NVFP4 row per half wavefront: lanes 0-31 encode one row, lanes 32-63 another. Lane g of a
+// half holds latent group g of its row (16 bf16 values as packed pairs: xa = values 0..7,
+// xb = values 8..15) and rope elements g (ra) and 32 + g (rb) as bf16 bits. The result is the
+// lane's 8 code bytes (row bytes 8g..8g+7) and, for g < 24, the row dword at byte 256 + 4g:
+// scale bytes 4g..4g+3 (g < 8), rope bytes 4(g-8).. (g < 16), rope bytes 32 + 4(g-16).. (else).
+// The scale byte is E4M3(amax * fl32(1/6)): for every finite bf16 amax this rounds to the same
+// byte as the exact quotient amax / 6 (checked exhaustively on the host). Every lane of the wave
+// must take part (the scale and rope bytes are gathered with lane shuffles).
+struct Nvfp4LaneOut {
+  uint32_t c0, c1, tail;
+};
+
+__device__ __forceinline__ Nvfp4LaneOut nvfp4_encode_lane(uint4v xa, uint4v xb, uint32_t ra, uint32_t rb) {
+  const int lane = threadIdx.x & 63;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_float(xa[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_bits_to_float(xa[i] >> 16);
+    v[8 + 2 * i] = bf16_bits_to_float(xb[i] & 0xFFFFu);
+    v[8 + 2 * i + 1] = bf16_bits_to_float(xb[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+  const uint32_t sbyte = e4m3_encode2_hw(amax * (1.0f / 6.0f), 0.0f) & 0xFFu;
+  const float sc = e4m3_to_float_hw(sbyte);
+  const float rinv = sc > 0.0f ? 1.0f / sc : 0.0f;          // IEEE division, once per group
+  const float bound = 8.0f * fmaxf(sc, 0x1p-20f);
+  Nvfp4LaneOut o;
+  o.c0 = e2m1_encode8_hw(v, sc, rinv, bound);              // elements 0..7
+  o.c1 = e2m1_encode8_hw(v + 8, sc, rinv, bound);          // elements 8..15
+  const uint32_t rpair = e4m3_encode2_hw(bf16_bits_to_float(ra), bf16_bits_to_float(rb));
+  const uint32_t rba = rpair & 0xFFu, rbb = rpair >> 8;
+  // scale dword k (groups 4k..4k+3) is built on lane 4k of the half, rope dword k (elements
+  // 4k..4k+3) on lane 4k (k < 8) or 4(k - 8) (k >= 8)
+  const uint32_t sword = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
+                         (__shfl_down(sbyte, 3) << 24);
+  const uint32_t rwa = rba | (__shfl_down(rba, 1) << 8) | (__shfl_down(rba, 2) << 16) |
+                       (__shfl_down(rba, 3) << 24);
+  const uint32_t rwb = rbb | (__shfl_down(rbb, 1) << 8) | (__shfl_down(rbb, 2) << 16) |
+                       (__shfl_down(rbb, 3) << 24);
+  const int src = (lane & 32) | (4 * (lane & 7));
+  const uint32_t w_s = __shfl(sword, src), w_a = __shfl(rwa, src), w_b = __shfl(rwb, src);
+  const int g = lane & 31;
+  o.tail = g < 8 ? w_s : (g < 16 ? w_a : w_b);
+  return o;
+}
+
 }  // namespace mla

@@ -40,6 +40,7 @@
 
 #include <type_traits>
 
+#include "codec_device.h"
 #include "mla_internal.h"
 #include "nvfp4_device.h"
 
@@ -155,9 +156,17 @@ constexpr int kProducers = 8;                                 // producer waves 
 // to 4 consecutive query tokens of one request over the union of their lists (a.u_pos), so a
 // row that several of them selected is gathered and decoded once; head block u belongs to token
 // 4g+u and its softmax masks the rows token 4g+u did not select (a.u_mask).
-template <int NH, bool DENSE, bool FP8, bool SH = false>
+// AP (fused append, NVFP4 sparse): while the producer waves compact the list (and note whether
+// an entry of it resolves to one of the request's new rows), the math waves encode the
+// request's q_len new rows with the quantize-append encoder. A workgroup whose list reads a new
+// row writes the rows to their cache slots and waits for its stores before its first gather, so
+// it reads the new bytes; one workgroup per request (token 0, split 0, first head group) writes
+// them in any case. Concurrent stores of several workgroups write the same bytes, so no
+// workgroup depends on another.
+template <int NH, bool DENSE, bool FP8, bool SH = false, bool AP = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
   static_assert(!SH || (NH == 4 && !DENSE && !FP8), "shared rows: NVFP4 sparse, 4 tokens");
+  static_assert(!AP || (!SH && !DENSE && !FP8), "fused append: NVFP4 sparse");
   constexpr int RB = FP8 ? kFp8RowBytes : kRowBytes;     // bytes per cache row
   __shared__ __attribute__((aligned(16))) uint8_t raw[FP8 ? 1 : kRawSlots][FP8 ? 16 : kRawTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t dec[kDecSlots][kDecTileBytes];
@@ -167,6 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   __shared__ uint32_t rowoff[DENSE ? kMaxDensePages : kMaxSplitRows];
   __shared__ __attribute__((aligned(4))) uint8_t rowmask[SH ? kMaxSplitRows : 4];   // SH: token bits
   __shared__ int32_t cnt_s[4][kProducers];
+  __shared__ __attribute__((aligned(16))) int32_t ap_hit_s[AP ? kProducers : 4];   // AP: per producer wave
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const bool math = w < 4;
@@ -234,6 +244,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
   };
 
+  // AP: the new rows' inputs, loaded by the math waves during the compaction
+  constexpr int kApPasses = AP ? (kApMaxRows / 2 + 3) / 4 : 1;     // row pairs per math wave
+  uint4v ap_xa[kApPasses], ap_xb[kApPasses];
+  uint32_t ap_ra[kApPasses], ap_rb[kApPasses];
+  int64_t ap_sl[kApPasses];
+
   // ---- rows of this split (producer waves) --------------------------------------------------
   int n_rows = 0;
   int p0 = 0;
@@ -272,6 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // Branch-free loads (clamped addresses, results selected afterwards) so that all index
       // loads are in flight together, then all block-table loads.
       int jv[4] = {-1, -1, -1, -1}, pg[4] = {-1, -1, -1, -1};
+      int64_t ap_slot = -1;
       if (cnt > 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -285,6 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
             jv[r] = (e < cnt) ? v : -1;
           }
         }
+        // AP: the slots of the request's new rows (lane k: row k), behind the index loads
+        if constexpr (AP) ap_slot = a.ap_slots[(int64_t)b * a.q_len + min(lane, a.q_len - 1)];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool in = jv[r] >= 0 && jv[r] < a.max_pages * kPageRows;
@@ -292,6 +311,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           pg[r] = in ? v : -1;
         }
       }
+      // AP: lane k < q_len holds the cache row (16-byte units) of the request's new row k
+      uint32_t ap_o16 = kInvalid;
+      if constexpr (AP) {
+        const int64_t off = ap_slot < 0 ? -1 : (ap_slot / kPageRows) * a.page_stride + (ap_slot % kPageRows) * kRowBytes;
+        if (lane < a.q_len && off >= 0 && off + kRowBytes <= a.cache_bytes) ap_o16 = (uint32_t)(off >> 4);
+      }
+      bool ap_hit = false;                    // AP: an entry of this lane reads a new row
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bool ok = false;
@@ -300,9 +326,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           const int64_t off = (int64_t)pg[r] * a.page_stride + (int64_t)(jv[r] & 63) * RB;
           if (off + RB <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
         }
+        if constexpr (AP) {
+          for (int k = 0; k < a.q_len; ++k) ap_hit |= ok && o16 == __builtin_amdgcn_readlane(ap_o16, k);
+        }
         const uint64_t mask = __ballot(ok);
         if (lane == 0) cnt_s[r][pw] = __popcll(mask);
         jv[r] = ok ? (int)o16 : -1;               // keep the offset (or -1) for the write below
+      }
+      if constexpr (AP) {
+        const uint64_t hits = __ballot(ap_hit);
+        if (lane == 0) ap_hit_s[pw] = hits != 0ull;
       }
       lds_barrier();
 #pragma unroll
@@ -325,6 +358,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         n_rows += total;
       }
     } else {
+      if constexpr (AP) {
+        // the new rows' inputs (pass i: rows 2p, 2p+1 with p = w + 4i), encoded after the
+        // barrier, while the producers finish the compaction
+#pragma unroll
+        for (int i = 0; i < kApPasses; ++i) {
+          const int p = w + 4 * i;
+          if (2 * p < a.q_len) {
+            const int64_t row = (int64_t)b * a.q_len + min(2 * p + (lane >> 5), a.q_len - 1);
+            const uint16_t* lrow = a.ap_latent + row * a.ap_latent_stride + 16 * (lane & 31);
+            ap_xa[i] = *(const uint4v*)lrow;
+            ap_xb[i] = *(const uint4v*)(lrow + 8);
+            ap_ra[i] = a.ap_rope[row * a.ap_rope_stride + (lane & 31)];
+            ap_rb[i] = a.ap_rope[row * a.ap_rope_stride + 32 + (lane & 31)];
+            ap_sl[i] = a.ap_slots[row];
+          }
+        }
+      }
       lds_barrier();
     }
   } else {
@@ -347,6 +397,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     dense_ok = __syncthreads_or(bad) == 0;
   }
   if (tid < 8) flag_s[tid >> 2][tid & 3] = 0;
+  if constexpr (AP) {
+    if (math) {
+      // Encode the request's new rows (lanes 0-31 row 2p, lanes 32-63 row 2p+1) and write them
+      // to their slots (as the append does: slots of -1 and slots outside the cache are not
+      // written) when the list reads one of them (then the stores complete before the barrier
+      // below, ahead of the first gathers) or when this is the request's writer workgroup.
+      const int half = lane >> 5, g = lane & 31;
+      const int4 h0 = *(const int4*)&ap_hit_s[0], h1 = *(const int4*)&ap_hit_s[4];
+      const bool hit = (h0.x | h0.y | h0.z | h0.w | h1.x | h1.y | h1.z | h1.w) != 0;
+      const bool store = hit || (split == 0 && rest % a.n_hg == 0 && a.head_begin == 0 && t == 0);
+#pragma unroll
+      for (int i = 0; i < kApPasses; ++i) {
+        const int k = 2 * (w + 4 * i) + half;
+        if (store && 2 * (w + 4 * i) < a.q_len) {
+          const Nvfp4LaneOut e = nvfp4_encode_lane(ap_xa[i], ap_xb[i], ap_ra[i], ap_rb[i]);
+          const int64_t slot = ap_sl[i];
+          const int64_t off = slot < 0 ? -1 : (slot / kPageRows) * a.page_stride + (slot % kPageRows) * kRowBytes;
+          if (k < a.q_len && off >= 0 && off + kRowBytes <= a.cache_bytes) {
+            uint8_t* dst = a.ap_cache + off;
+            *(uint2v*)(dst + 8 * g) = uint2v{e.c0, e.c1};
+            if (g < 24) ((uint32_t*)(dst + kScaleOff))[g] = e.tail;
+          }
+        }
+      }
+      if (hit) wait_vmcnt<0>();
+    }
+  }
   if constexpr (!DENSE) {
     // the math waves learn the row count from the per-wave counts
     if (math) {
@@ -426,6 +503,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       return (ok && pb != kInvalid && o * 16 + RB <= a.cache_bytes) ? (uint32_t)o : kInvalid;
     }
   };
+  // Source of byte pb of a row: the cache or the zero row.
+  auto gather_src = [&](uint32_t o16, uint32_t pb) -> const uint8_t* {
+    return (o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 + pb : g_zero_row + pb;
+  };
   auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) o16[k] = row_o16(tile * kTileRows + (int)(pk[k] >> 16));
@@ -436,8 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     for (int k = 0; k < 3; ++k) {
       if (k >= nk) break;
       const uint32_t pb = pk[k] & 0xFFFFu;
-      const uint8_t* src = (o16[k] != kInvalid) ? a.cache + (int64_t)o16[k] * 16 + pb : g_zero_row + pb;
-      gather16_to_lds(src, dst + (k * 256 + w * 64) * 16);
+      gather16_to_lds(gather_src(o16[k], pb), dst + (k * 256 + w * 64) * 16);
     }
   };
   // Wait until the gathers issued before the last `after` tiles have landed in LDS.
@@ -659,8 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           const int q = k * 512 + ptid;
           const uint32_t pb = (uint32_t)((q % 22) * 16);
           const uint32_t o16 = row_o16(tile * kTileRows + q / 22);
-          const uint8_t* src = (o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 + pb : g_zero_row + pb;
-          gather16_to_lds(src, raw[tile % kRawSlots] + (k * 512 + pw * 64) * 16);
+          gather16_to_lds(gather_src(o16, pb), raw[tile % kRawSlots] + (k * 512 + pw * 64) * 16);
         }
       };
       prod_issue(0);
@@ -875,6 +954,17 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
 
 hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream) {
   const dim3 grid((unsigned)a.items_per_xcd * 8), block(kThreads);
+  if (a.ap_slots) {                           // fused append: NVFP4 sparse only
+    if (dense || fp8) return hipErrorInvalidValue;
+    switch (nh) {
+      case 1: hipLaunchKernelGGL((decode_kernel<1, false, false, false, true>), grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((decode_kernel<2, false, false, false, true>), grid, block, 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((decode_kernel<3, false, false, false, true>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((decode_kernel<4, false, false, false, true>), grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
 #define MLA_LAUNCH(NHV, DV, FV) \
   hipLaunchKernelGGL((decode_kernel<NHV, DV, FV>), grid, block, 0, stream, a)
 #define MLA_CASES(FV)                           \

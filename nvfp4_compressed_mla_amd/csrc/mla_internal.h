@@ -40,7 +40,18 @@ struct DecodeArgs {
   const int32_t* u_count;   // [n_groups, kUnionParts] entries of each part
   int32_t u_stride;
   int32_t groups_per_req;   // ceil(q_len / 4)
+  // Fused append (sparse NVFP4 rows only; ap_slots != null selects it): every workgroup of a
+  // request encodes the request's q_len new rows (row b*q_len + t: bf16 latent and rope, cache
+  // slot) and writes them to their cache slots before its first gather.
+  const uint16_t* ap_latent;    // [T, ap_latent_stride] bf16
+  int64_t ap_latent_stride;
+  const uint16_t* ap_rope;      // [T, ap_rope_stride] bf16
+  int64_t ap_rope_stride;
+  const int64_t* ap_slots;      // [T] flat cache slots (page * 64 + row), -1 = not written
+  uint8_t* ap_cache;            // the cache (written)
 };
+
+constexpr int kApMaxRows = 16;                                  // q_len limit of the fused append
 
 constexpr int kMaxSplitRows = 2048;   // sparse rows per split held in LDS
 constexpr int kMaxDensePages = 128;   // dense pages per split held in LDS (8192 positions)

@@ -288,3 +288,24 @@ def test_shared_decode_entry_points(lib):
     assert call(ws=None) == WORKSPACE
     assert call(wb=1024) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE
+
+
+def test_fused_append_decode_entry_point_rejects(lib):
+    f = lib.mla_sparse_decode_append
+    args = dict(q=FAKE, qd=0, c=FAKE, stride=22528, cb=22528 * 4, bt=FAKE, mp=4, idx=FAKE, k=256,
+                B=1, ql=2, H=16, sc=0.04, S=2, lat=FAKE, ls=512, rope=FAKE, rs=64, slots=FAKE,
+                out=FAKE, lse=None, ws=FAKE, wb=1 << 30)
+
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return f(a["q"], a["qd"], a["c"], a["stride"], a["cb"], a["bt"], a["mp"], a["idx"], a["k"],
+                 a["B"], a["ql"], a["H"], a["sc"], a["S"], a["lat"], a["ls"], a["rope"], a["rs"],
+                 a["slots"], a["out"], a["lse"], a["ws"], a["wb"], None)
+    assert call(lat=None) == INVALID and call(rope=None) == INVALID and call(slots=None) == INVALID
+    assert call(ls=500) == INVALID and call(rs=32) == INVALID
+    assert call(lat=ctypes.c_void_p(0x10008)) == INVALID           # latent not 16-byte aligned
+    assert call(slots=ctypes.c_void_p(0x10004)) == INVALID         # slots not 8-byte aligned
+    assert call(ql=17) == UNSUPPORTED                              # q_len above 16
+    assert call(ws=None) == WORKSPACE                              # two splits keep partials
+    assert call(wb=1024) == WORKSPACE
+    assert call(idx=None) == INVALID and call(k=2049) == UNSUPPORTED
