@@ -37,7 +37,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batched_counters.txt")
 SPIN_CYCLES = 2_000_000          # GPU spin before a timed region (about a millisecond)
 HEAT_MS = 30.0                   # GPU work replayed before the warmup of every timed region
 KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_compressed_mla_amd", "csrc", f)
-                  for f in ("decode.hip", "nvfp4_device.h")]
+                  for f in ("decode.hip", "nvfp4_device.h", "codec_device.h", "mla_internal.h")]
 
 
 def log(msg):
@@ -787,9 +787,11 @@ def main():
             "mfma_TFLOPs": round(flops / (kavg * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
             "kernel_source_sha256_16": src_hash,
-            "timing_note": "kernel_us comes from HIP events the library records around the fused "
-                           "kernel on its launch stream (eager launches); against the rocprofv3 "
-                           "kernel trace they include about 1-3 us of command-packet time",
+            "timing_note": "kernel_us comes from HIP events the library records at the fused "
+                           "kernel's own start and end (hipExtLaunchKernel's events, on its launch "
+                           "stream), over eager launches that each follow some idle time; the "
+                           "rocprofv3 trace average, dominated by back-to-back graph replays, is "
+                           "about 2 us lower (profiles/decode_batched_kernel_trace.txt)",
         },
         "roofline_launch": {
             "bound": "hbm",

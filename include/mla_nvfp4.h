@@ -359,9 +359,10 @@ mla_status mla_nvfp4_dequantize_rows(const void* kv_cache, int64_t page_stride_b
 
 /* Profiling hook, off the hot path: when `start`/`stop` are non-null, every later
  * mla_sparse_decode / mla_dense_decode call on this host thread records `start` on its stream
- * right before the fused decode kernel(s) and `stop` right after them (before the split-combine
- * kernel), so hipEventElapsedTime gives the fused kernel's own duration. Pass nulls to turn it
- * off. The events are owned by the caller; they must not be recorded inside a graph capture. */
+ * at the start of the (first) fused decode kernel and `stop` at the end of the (last) one, before
+ * the split-combine kernel (hipExtLaunchKernel's kernel-boundary events), so hipEventElapsedTime
+ * gives the fused kernel's own duration. Pass nulls to turn it off. The events are owned by the
+ * caller; they must not be recorded inside a graph capture. */
 mla_status mla_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 const char* mla_status_string(mla_status s);

@@ -131,13 +131,11 @@ mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, bool fp8, hipStr
   const int64_t T = (int64_t)a.B * a.q_len;
   const int32_t S = a.n_split;
   const int32_t T32 = (int32_t)T;
-  if (g_timing_start) {
-    hipError_t e = hipEventRecord(g_timing_start, stream);
-    if (e != hipSuccess) return hip_status(e, "timing start event");
-  }
   const int32_t nb = H / 16;
   const int32_t full = nb / 4, tail = nb % 4;
-  // launch 1: groups of 64 heads; launch 2: the remaining 16..48 heads
+  // launch 1: groups of 64 heads; launch 2: the remaining 16..48 heads. The timing events (if
+  // set) are recorded at the start of the first decode kernel and the end of the last.
+  const int first = full > 0 ? 0 : 1, last = tail > 0 ? 1 : 0;
   for (int part = 0; part < 2; ++part) {
     const int32_t nh = part == 0 ? 4 : tail;
     const int32_t groups = part == 0 ? full : (tail ? 1 : 0);
@@ -146,12 +144,9 @@ mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, bool fp8, hipStr
     a.n_hg = groups;
     a.total_items = T32 * groups * S;
     a.items_per_xcd = (a.total_items + 7) / 8;
-    hipError_t e = mla::launch_decode(a, nh, dense, fp8, stream);
+    hipError_t e = mla::launch_decode(a, nh, dense, fp8, stream, part == first ? g_timing_start : nullptr,
+                                      part == last ? g_timing_stop : nullptr);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");
-  }
-  if (g_timing_stop) {
-    hipError_t e = hipEventRecord(g_timing_stop, stream);
-    if (e != hipSuccess) return hip_status(e, "timing stop event");
   }
   if (S > 1) {
     hipError_t e = mla::launch_combine(T32, H, S, a.ws_o, a.ws_lse, a.out, a.lse, stream);
@@ -619,16 +614,9 @@ mla_status mla_sparse_decode_shared(const void* q, mla_dtype q_dtype, const void
   hipError_t e = mla::launch_union(topk_idx, topk, B, q_len, max_pages * MLA_PAGE_ROWS, (int32_t*)ws,
                                    ws + l.mask, (int32_t*)(ws + l.count), l.stride, stream);
   if (e != hipSuccess) return hip_status(e, "union kernel launch");
-  if (g_timing_start) {                       // the timing hook brackets the decode kernel only
-    e = hipEventRecord(g_timing_start, stream);
-    if (e != hipSuccess) return hip_status(e, "timing start event");
-  }
-  e = mla::launch_decode_shared(a, stream);
+  // the timing hook brackets the decode kernel only
+  e = mla::launch_decode_shared(a, stream, g_timing_start, g_timing_stop);
   if (e != hipSuccess) return hip_status(e, "shared decode kernel launch");
-  if (g_timing_stop) {
-    e = hipEventRecord(g_timing_stop, stream);
-    if (e != hipSuccess) return hip_status(e, "timing stop event");
-  }
   if (l.S > 1) {
     e = mla::launch_combine((int32_t)T, H, l.S, a.ws_o, a.ws_lse, out, lse, stream);
     if (e != hipSuccess) return hip_status(e, "combine kernel launch");

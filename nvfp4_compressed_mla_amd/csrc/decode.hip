@@ -35,6 +35,7 @@
 // split the kernel writes the final output.
 // Workgroup i is placed on XCD i % 8 by the hardware; items are remapped so that the splits of
 // one token are consecutive on one XCD and share its L2.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -456,9 +457,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
             for (int n = 0; n < 4; ++n) dst[16 * n] = 0.0f;
           }
         } else {
-          _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+          _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 16 + 2 * pw) * 512 + 8 * lane;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) *(uint2v*)(dst + 256 * n) = uint2v{0u, 0u};
+          for (int m = 0; m < 2; ++m) *(uint4v*)(dst + 512 * m) = uint4v{0u, 0u, 0u, 0u};
         }
         if (pw == 0 && l16 == 0) {
 #pragma unroll
@@ -826,22 +827,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int n = 0; n < 4; ++n) dst[16 * n] = o[hb][n][e] * inv[e];
         }
       } else {
-        // FP16 partial in register order: [token][split][16-head block][dim block][lane][4 heads].
-        // With at most kStreamPartialSplits splits the partials are written with streaming
+        // FP16 partial in register order: [token][split][16-head block][pair of 16-dim blocks]
+        // [lane][2 dim blocks][4 heads], so that each lane stores 16 bytes at a time (dim blocks
+        // 4pw + 2m and 4pw + 2m + 1 of its 4 heads). With at most kStreamPartialSplits splits the partials are written with streaming
         // (non-temporal) stores: they then leave no dirty lines for the end-of-kernel L2
         // write-back, which shortens this kernel by more than the combine, whose single round of
         // loads then reads them from the memory-side cache, loses. With more splits the combine
         // reads in several rounds and the partials are better kept in the L2.
-        _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 32 + 4 * pw) * 256 + 4 * lane;
+        _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 16 + 2 * pw) * 512 + 8 * lane;
         const bool stream = a.n_split <= kStreamPartialSplits;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const float4v v = o[hb][n] * inv;
-          const half4v hv = half4v{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        for (int m = 0; m < 2; ++m) {
+          const float4v v0 = o[hb][2 * m] * inv, v1 = o[hb][2 * m + 1] * inv;
+          const half8v hv = half8v{(_Float16)v0[0], (_Float16)v0[1], (_Float16)v0[2], (_Float16)v0[3],
+                                   (_Float16)v1[0], (_Float16)v1[1], (_Float16)v1[2], (_Float16)v1[3]};
           if (stream)
-            __builtin_nontemporal_store(__builtin_bit_cast(uint2v, hv), (uint2v*)(dst + 256 * n));
+            __builtin_nontemporal_store(__builtin_bit_cast(uint4v, hv), (uint4v*)(dst + 512 * m));
           else
-            *(half4v*)(dst + 256 * n) = hv;
+            *(half8v*)(dst + 512 * m) = hv;
         }
       }
       if (pw == 0 && l16 == 0) {
@@ -863,9 +866,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
 // Merge the n_split partial (o_s, lse_s) of each (token, head) in split order:
 // M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
-// A thread owns one dim of 4 heads, the 8-byte FP16 unit the decode kernel stored. SC > 0 handles
-// up to SC splits with every load issued in one round (one memory latency); SC == 0 handles any
-// split count, 8 splits at a time.
+// A thread owns two dims (16 apart) of 4 heads, the 16-byte FP16 unit the decode kernel stored.
+// SC > 0 handles up to SC splits with every load issued in one round (one memory latency);
+// SC == 0 handles any split count, 8 splits at a time.
 constexpr int kCombineChunk = 8;
 
 template <int SC>
@@ -875,39 +878,40 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse,
                                                       int32_t per_xcd, int32_t total) {
-  // block = (token, 16-head block, 4 dim blocks); thread = (dim block, lane)
+  // block = (token, 16-head block, 4 pairs of dim blocks); thread = (pair, lane)
   const int hw = blockIdx.x;
   const int L = (hw & 7) * per_xcd + (hw >> 3);
   if (L >= total) return;
   const int nhb = H >> 4;
-  const int tok = L / (nhb * 8);
-  const int r = L % (nhb * 8);
-  const int hb = r >> 3;
-  const int ng = (r & 7) * 4 + (threadIdx.x >> 6);
+  const int tok = L / (nhb * 4);
+  const int r = L % (nhb * 4);
+  const int hb = r >> 2;
+  const int q = (r & 3) * 4 + (threadIdx.x >> 6);          // pair of dim blocks 2q, 2q + 1
   const int lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
   const int head = 16 * hb + 4 * kg;                      // heads head..head+3
   const int64_t split_stride = (int64_t)H * kLatent;
-  const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 32 + ng) * 64 + lane) * 4;
+  const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 16 + q) * 64 + lane) * 8;
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
   const float4v ninf = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float4v M = ninf;
-  float4v acc = float4v{0.f, 0.f, 0.f, 0.f}, wsum = acc;
-  auto merge = [&](const float4v& ls, const half4v& hv) {
+  float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0, wsum = acc0;
+  auto merge = [&](const float4v& ls, const half8v& hv) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float wgt = (ls[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((ls[e] - M[e]) * 1.4426950408889634f);
-      acc[e] += wgt * (float)hv[e];
+      acc0[e] += wgt * (float)hv[e];
+      acc1[e] += wgt * (float)hv[4 + e];
       wsum[e] += wgt;
     }
   };
   if constexpr (SC > 0) {
     float4v ls[SC];
-    half4v ov[SC];
+    half8v ov[SC];
 #pragma unroll
     for (int j = 0; j < SC; ++j) {
       const int s = min(j, S - 1);                        // splits past S: weight 0
       ls[j] = (j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
-      ov[j] = *(const half4v*)(op + s * split_stride);
+      ov[j] = *(const half8v*)(op + s * split_stride);
     }
 #pragma unroll
     for (int j = 0; j < SC; ++j)
@@ -928,12 +932,12 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
     }
     for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
       float4v ls[kCombineChunk];
-      half4v ov[kCombineChunk];
+      half8v ov[kCombineChunk];
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j) {
         const int s = min(s0 + j, S - 1);
         ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
-        ov[j] = *(const half4v*)(op + s * split_stride);
+        ov[j] = *(const half8v*)(op + s * split_stride);
       }
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j) merge(ls[j], ov[j]);
@@ -942,9 +946,11 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
-    out[((int64_t)tok * H + head + e) * kLatent + 16 * ng + l16] = acc[e] * inv;
+    float* o = out + ((int64_t)tok * H + head + e) * kLatent + 32 * q + l16;
+    o[0] = acc0[e] * inv;
+    o[16] = acc1[e] * inv;
   }
-  if (lse && ng == 0 && l16 == 0) {
+  if (lse && q == 0 && l16 == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       lse[(int64_t)tok * H + head + e] =
@@ -952,21 +958,25 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   const dim3 grid((unsigned)a.items_per_xcd * 8), block(kThreads);
   if (a.ap_slots) {                           // fused append: NVFP4 sparse only
     if (dense || fp8) return hipErrorInvalidValue;
+#define MLA_LAUNCH_AP(NHV) \
+  hipExtLaunchKernelGGL((decode_kernel<NHV, false, false, false, true>), grid, block, 0, stream, ev_start, ev_stop, 0, a)
     switch (nh) {
-      case 1: hipLaunchKernelGGL((decode_kernel<1, false, false, false, true>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((decode_kernel<2, false, false, false, true>), grid, block, 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((decode_kernel<3, false, false, false, true>), grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((decode_kernel<4, false, false, false, true>), grid, block, 0, stream, a); break;
+      case 1: MLA_LAUNCH_AP(1); break;
+      case 2: MLA_LAUNCH_AP(2); break;
+      case 3: MLA_LAUNCH_AP(3); break;
+      case 4: MLA_LAUNCH_AP(4); break;
       default: return hipErrorInvalidValue;
     }
+#undef MLA_LAUNCH_AP
     return hipGetLastError();
   }
 #define MLA_LAUNCH(NHV, DV, FV) \
-  hipLaunchKernelGGL((decode_kernel<NHV, DV, FV>), grid, block, 0, stream, a)
+  hipExtLaunchKernelGGL((decode_kernel<NHV, DV, FV>), grid, block, 0, stream, ev_start, ev_stop, 0, a)
 #define MLA_CASES(FV)                           \
   switch (nh * 2 + (dense ? 1 : 0)) {           \
     case 2: MLA_LAUNCH(1, false, FV); break;    \
@@ -989,15 +999,16 @@ hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<4, false, false, true>), dim3((unsigned)a.items_per_xcd * 8),
-                     dim3(kThreads), 0, stream, a);
+hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream, hipEvent_t ev_start,
+                                hipEvent_t ev_stop) {
+  hipExtLaunchKernelGGL((decode_kernel<4, false, false, true>), dim3((unsigned)a.items_per_xcd * 8),
+                        dim3(kThreads), 0, stream, ev_start, ev_stop, 0, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
-  const int32_t total = T * (H / 16) * 8;
+  const int32_t total = T * (H / 16) * 4;
   const int32_t per_xcd = (total + 7) / 8;
   if (n_split <= 8)
     hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,

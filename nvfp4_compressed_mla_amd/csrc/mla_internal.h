@@ -30,7 +30,7 @@ struct DecodeArgs {
   int32_t items_per_xcd;    // ceil(total_items / 8)
   float* out;               // [T, H, 512] (n_split == 1)
   float* lse;               // [T, H] or null (n_split == 1)
-  _Float16* ws_o;           // [T, n_split, H/16, 32, 64, 4] FP16 partial outputs (n_split > 1)
+  _Float16* ws_o;           // [T, n_split, H/16, 16, 64, 2, 4] FP16 partial outputs (n_split > 1)
   float* ws_lse;            // [T, n_split, H] partial log-sum-exp (natural log)
   // Shared-row mode (the rows selected by a group of up to 4 consecutive query tokens of one
   // request, deduplicated): workgroup = (group, 16-head block, split), head block u of the
@@ -65,12 +65,15 @@ hipError_t launch_dequantize_rows(const void* cache, int64_t page_stride, int64_
                                   const int64_t* slots, int64_t n, float* out, hipStream_t stream);
 
 // nh = heads per workgroup / 16 (1..4); dense selects implicit positions; fp8 selects 576-byte
-// FP8 rows instead of 352-byte NVFP4 rows.
-hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream);
+// FP8 rows instead of 352-byte NVFP4 rows. ev_start / ev_stop (may be null) are recorded at the
+// kernel's start and end.
+hipError_t launch_decode(const DecodeArgs& a, int nh, bool dense, bool fp8, hipStream_t stream,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Shared-row decode (NVFP4 rows, 4 tokens x 16 heads per workgroup) over the unions built by
 // launch_union.
-hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream,
+                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Union of the index lists of each group of up to 4 consecutive query tokens of a request:
 // ascending distinct positions in [0, n_pos) and their 4-bit token masks, in kUnionParts parts
