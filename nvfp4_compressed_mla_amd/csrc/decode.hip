@@ -829,11 +829,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       } else {
         // FP16 partial in register order: [token][split][16-head block][pair of 16-dim blocks]
         // [lane][2 dim blocks][4 heads], so that each lane stores 16 bytes at a time (dim blocks
-        // 4pw + 2m and 4pw + 2m + 1 of its 4 heads). With at most kStreamPartialSplits splits the partials are written with streaming
-        // (non-temporal) stores: they then leave no dirty lines for the end-of-kernel L2
-        // write-back, which shortens this kernel by more than the combine, whose single round of
-        // loads then reads them from the memory-side cache, loses. With more splits the combine
-        // reads in several rounds and the partials are better kept in the L2.
+        // 4pw + 2m and 4pw + 2m + 1 of its 4 heads). With at most kStreamPartialSplits splits the
+        // partials are written with streaming (non-temporal) stores: they then leave no dirty
+        // lines for the end-of-kernel L2 write-back, which shortens this kernel by more than the
+        // combine, whose single round of loads then reads them from the memory-side cache, loses.
+        // With more splits the combine reads in several rounds and the partials are better kept
+        // in the L2.
         _Float16* dst = a.ws_o + (((otok * a.n_split + split) * (a.H >> 4) + hbg) * 16 + 2 * pw) * 512 + 8 * lane;
         const bool stream = a.n_split <= kStreamPartialSplits;
 #pragma unroll
