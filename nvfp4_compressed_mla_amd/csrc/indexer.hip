@@ -48,6 +48,8 @@ __device__ __forceinline__ float idx_group4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+__device__ __forceinline__ float idx_relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.4028234663852886e38f); }
+
 __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerArgs a) {
   // key r, 16-byte piece c (dims 16c..16c+15) at r*128 + 16*(c ^ (r & 7))
   __shared__ __attribute__((aligned(16))) uint8_t keys[kIdxBlockRows * kIndexerDim];
@@ -114,16 +116,19 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerAr
     const __amdgpu_buffer_rsrc_t out_rs =
         __builtin_amdgcn_make_buffer_rsrc(a.scores + tok * a.n_max + p0, (short)0, nr * 4, 0x00020000);
     const int n_kt = (nr + 15) >> 4;
+    // The key rows a lane reads step by 16, so their swizzle (row & 7 = l16 & 7) is fixed.
+    const int koff0 = ((2 * kg) ^ (l16 & 7)) << 4, koff1 = ((2 * kg + 1) ^ (l16 & 7)) << 4;
     // two 16-position tiles per step: 8 independent MFMAs, then their epilogues
     for (int kt0 = 0; kt0 < n_kt; kt0 += 2) {
       f32x4 d[2][4];
       int rr[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        rr[u] = min((kt0 + u) * 16 + l16, kIdxBlockRows - 1);    // (a tile past n_kt is not stored)
+        // a tile past n_kt (not stored) reads the last row's bytes at this lane's offsets
+        rr[u] = min((kt0 + u) * 16 + l16, kIdxBlockRows - 1);
         const uint8_t* kr = keys + rr[u] * kIndexerDim;
-        const uint4 k0 = *(const uint4*)(kr + (((2 * kg) ^ (rr[u] & 7)) << 4));
-        const uint4 k1 = *(const uint4*)(kr + (((2 * kg + 1) ^ (rr[u] & 7)) << 4));
+        const uint4 k0 = *(const uint4*)(kr + koff0);
+        const uint4 k1 = *(const uint4*)(kr + koff1);
         const i32x8 kb = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
@@ -133,12 +138,14 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerAr
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        // ReLU as one v_med3_f32 (fmaxf would add a NaN-canonicalising max: the dot products are
+        // sums of exact products of finite E4M3 values, never NaN)
         float sh[4];
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-          sh[hb] = wv[hb][0] * fmaxf(d[u][hb][0], 0.0f);
+          sh[hb] = wv[hb][0] * idx_relu(d[u][hb][0]);
 #pragma unroll
-          for (int e = 1; e < 4; ++e) sh[hb] = __builtin_fmaf(wv[hb][e], fmaxf(d[u][hb][e], 0.0f), sh[hb]);
+          for (int e = 1; e < 4; ++e) sh[hb] = __builtin_fmaf(wv[hb][e], idx_relu(d[u][hb][e]), sh[hb]);
         }
         const float s = idx_group4_sum((sh[0] + sh[1]) + (sh[2] + sh[3])) * kscale[rr[u]];
         const int r = (kt0 + u) * 16 + l16;
