@@ -825,6 +825,19 @@ def main():
             extra[key] = run_config(w2, 192, 24, 32)
             del w2
             torch.cuda.empty_cache()
+        if "mtp" in wanted:
+            # an MTP decode step that appends its 15 new rows per request (one per query token):
+            # append kernel + decode against the fused call, same inputs, graph-replayed steps
+            log("[bench] extra: mtp_B16_q15_H64 with its own 15 rows per request appended")
+            w2 = SparseWorkload("mtp_append", 16, 15, 64, [149504] * 16, 2048, 15, 6, 1012, dev)
+            sep = time_steps(w2.step, w2.rot, 48, 6)
+            w2.use_fused_append()
+            fus = time_steps(w2.step, w2.rot, 48, 6)
+            extra["mtp_B16_q15_H64_step_with_append"] = {
+                "append_then_decode_us": round(sep * 1e3, 2), "fused_us": round(fus * 1e3, 2),
+                "appended_rows": 16 * 15}
+            del w2
+            torch.cuda.empty_cache()
         if "dense" in wanted:
             log("[bench] extra: dense_B8_H64_146K")
             dw = DenseWorkload(8, 64, 149504, 4096, 3, 1003, dev)

@@ -157,13 +157,13 @@ constexpr int kProducers = 8;                                 // producer waves 
 // to 4 consecutive query tokens of one request over the union of their lists (a.u_pos), so a
 // row that several of them selected is gathered and decoded once; head block u belongs to token
 // 4g+u and its softmax masks the rows token 4g+u did not select (a.u_mask).
-// AP (fused append, NVFP4 sparse): while the producer waves compact the list (and note whether
-// an entry of it resolves to one of the request's new rows), the math waves encode the
-// request's q_len new rows with the quantize-append encoder. A workgroup whose list reads a new
-// row writes the rows to their cache slots and waits for its stores before its first gather, so
-// it reads the new bytes; one workgroup per request (token 0, split 0, first head group) writes
-// them in any case. Concurrent stores of several workgroups write the same bytes, so no
-// workgroup depends on another.
+// AP (fused append, NVFP4 sparse): while the producer waves compact the list (and note which of
+// the request's new rows its entries resolve to), the math waves load the request's q_len new
+// rows. A workgroup whose list reads new rows encodes them with the quantize-append encoder and
+// writes them to their cache slots; its stores complete before it gathers those rows, so it
+// reads the new bytes. One workgroup per request (token 0, split 0, first head group) encodes
+// and writes all of them, which is the append itself. Concurrent stores of several workgroups
+// write the same bytes, so no workgroup depends on another.
 template <int NH, bool DENSE, bool FP8, bool SH = false, bool AP = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
   static_assert(!SH || (NH == 4 && !DENSE && !FP8), "shared rows: NVFP4 sparse, 4 tokens");
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   __shared__ __attribute__((aligned(4))) uint8_t rowmask[SH ? kMaxSplitRows : 4];   // SH: token bits
   __shared__ int32_t cnt_s[4][kProducers];
   __shared__ __attribute__((aligned(16))) int32_t ap_hit_s[AP ? kProducers : 4];   // AP: per producer wave
+  __shared__ __attribute__((aligned(16))) int32_t ap_early_s[AP ? kProducers : 4];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const bool math = w < 4;
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // loads are in flight together, then all block-table loads.
       int jv[4] = {-1, -1, -1, -1}, pg[4] = {-1, -1, -1, -1};
       int64_t ap_slot = -1;
+      bool ap_early = false;
       if (cnt > 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -312,13 +314,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           pg[r] = in ? v : -1;
         }
       }
-      // AP: lane k < q_len holds the cache row (16-byte units) of the request's new row k
-      uint32_t ap_o16 = kInvalid;
+      // AP: lane k < q_len holds the cache row (16-byte units) of the request's new row k;
+      // [ap_lo, ap_hi] spans them (an entry outside it reads none of them)
+      uint32_t ap_o16 = kInvalid, ap_lo = kInvalid, ap_hi = 0u;
       if constexpr (AP) {
         const int64_t off = ap_slot < 0 ? -1 : (ap_slot / kPageRows) * a.page_stride + (ap_slot % kPageRows) * kRowBytes;
         if (lane < a.q_len && off >= 0 && off + kRowBytes <= a.cache_bytes) ap_o16 = (uint32_t)(off >> 4);
+        for (int k = 0; k < a.q_len; ++k) {
+          const uint32_t nk = __builtin_amdgcn_readlane(ap_o16, k);
+          if (nk != kInvalid) { ap_lo = min(ap_lo, nk); ap_hi = max(ap_hi, nk); }
+        }
       }
-      bool ap_hit = false;                    // AP: an entry of this lane reads a new row
+      uint32_t ap_hits = 0u;                  // AP: bit k: an entry of this wave reads new row k
+      bool ap_hit_r[4] = {false, false, false, false};   // AP: entry r of this lane reads a new row
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bool ok = false;
@@ -328,15 +336,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           if (off + RB <= a.cache_bytes) { ok = true; o16 = (uint32_t)(off >> 4); }
         }
         if constexpr (AP) {
-          for (int k = 0; k < a.q_len; ++k) ap_hit |= ok && o16 == __builtin_amdgcn_readlane(ap_o16, k);
+          // the full comparison only in a wave with an entry inside the new rows' span
+          if (__ballot(ok && o16 >= ap_lo && o16 <= ap_hi) != 0ull) {
+            for (int k = 0; k < a.q_len; ++k) {
+              const bool h = ok && o16 == __builtin_amdgcn_readlane(ap_o16, k);
+              ap_hit_r[r] = ap_hit_r[r] || h;
+              if (__ballot(h) != 0ull) ap_hits |= 1u << k;
+            }
+          }
         }
         const uint64_t mask = __ballot(ok);
         if (lane == 0) cnt_s[r][pw] = __popcll(mask);
         jv[r] = ok ? (int)o16 : -1;               // keep the offset (or -1) for the write below
       }
       if constexpr (AP) {
-        const uint64_t hits = __ballot(ap_hit);
-        if (lane == 0) ap_hit_s[pw] = hits != 0ull;
+        if (lane == 0) ap_hit_s[pw] = (int32_t)ap_hits;
       }
       lds_barrier();
 #pragma unroll
@@ -356,7 +370,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           rowoff[n_rows + before + below] = (uint32_t)jv[r];
           if constexpr (SH) rowmask[n_rows + before + below] = (uint8_t)mk[r];
         }
+        // AP: a new row among the first kRawSlots tiles, which the producers gather right after
+        // the prologue barrier
+        if constexpr (AP) ap_early = ap_early || (ok && ap_hit_r[r] && (int)(n_rows + before + below) < kRawSlots * kTileRows);
         n_rows += total;
+      }
+      if constexpr (AP) {
+        const uint64_t early = __ballot(ap_early);
+        if (lane == 0) ap_early_s[pw] = early != 0ull;
       }
     } else {
       if constexpr (AP) {
@@ -402,27 +423,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (math) {
       // Encode the request's new rows (lanes 0-31 row 2p, lanes 32-63 row 2p+1) and write them
       // to their slots (as the append does: slots of -1 and slots outside the cache are not
-      // written) when the list reads one of them (then the stores complete before the barrier
-      // below, ahead of the first gathers) or when this is the request's writer workgroup.
+      // written): the rows the list reads, and every row in the request's writer workgroup.
+      // The stores complete before any gather of those rows: a math wave's vector-memory
+      // operations complete in issue order, so its query loads after the next barrier wait for
+      // them, and the gathers of tile 3 onwards come after the prologue barriers that follow;
+      // when a new row is among the first tiles, which the producers gather right after the next
+      // barrier, the workgroup waits for the stores and takes one barrier more (below).
       const int half = lane >> 5, g = lane & 31;
       const int4 h0 = *(const int4*)&ap_hit_s[0], h1 = *(const int4*)&ap_hit_s[4];
-      const bool hit = (h0.x | h0.y | h0.z | h0.w | h1.x | h1.y | h1.z | h1.w) != 0;
-      const bool store = hit || (split == 0 && rest % a.n_hg == 0 && a.head_begin == 0 && t == 0);
+      const uint32_t hits = (uint32_t)(h0.x | h0.y | h0.z | h0.w | h1.x | h1.y | h1.z | h1.w);
+      const bool writer = split == 0 && rest % a.n_hg == 0 && a.head_begin == 0 && t == 0;
+      const uint32_t rows = writer ? 0xFFFFFFFFu : hits;       // rows this workgroup stores
 #pragma unroll
       for (int i = 0; i < kApPasses; ++i) {
-        const int k = 2 * (w + 4 * i) + half;
-        if (store && 2 * (w + 4 * i) < a.q_len) {
+        const int k0 = 2 * (w + 4 * i), k = k0 + half;
+        if (((rows >> k0) & 3u) != 0u && k0 < a.q_len) {
           const Nvfp4LaneOut e = nvfp4_encode_lane(ap_xa[i], ap_xb[i], ap_ra[i], ap_rb[i]);
           const int64_t slot = ap_sl[i];
           const int64_t off = slot < 0 ? -1 : (slot / kPageRows) * a.page_stride + (slot % kPageRows) * kRowBytes;
-          if (k < a.q_len && off >= 0 && off + kRowBytes <= a.cache_bytes) {
+          if (((rows >> k) & 1u) != 0u && k < a.q_len && off >= 0 && off + kRowBytes <= a.cache_bytes) {
             uint8_t* dst = a.ap_cache + off;
             *(uint2v*)(dst + 8 * g) = uint2v{e.c0, e.c1};
             if (g < 24) ((uint32_t*)(dst + kScaleOff))[g] = e.tail;
           }
         }
       }
-      if (hit) wait_vmcnt<0>();
     }
   }
   if constexpr (!DENSE) {
@@ -441,6 +466,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // positions): every wave knows n_rows here, so the workgroup leaves together. The result is the
   // softmax over no rows, written by the producer waves in the epilogue's layout: zero outputs
   // and lse = -inf. No query load or gather has been issued yet.
+  if constexpr (AP) {
+    // a new row among the first tiles: its stores complete before the producers gather them
+    const int4 e0 = *(const int4*)&ap_early_s[0], e1 = *(const int4*)&ap_early_s[4];
+    if ((e0.x | e0.y | e0.z | e0.w | e1.x | e1.y | e1.z | e1.w) != 0) {
+      if (math) wait_vmcnt<0>();
+      lds_barrier();
+    }
+  }
   if (n_rows == 0) {
     if (!math) {
       const bool final_out = (a.n_split == 1);
@@ -537,6 +570,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     load_q();
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) asm volatile("" : "+v"(qf[c]));
+    // AP: this wave's new-row stores are complete before any math wave gathers tile 3 (a wave
+    // that loads queries has already waited for them: its operations complete in order)
+    if constexpr (AP) wait_vmcnt<0>();
     lds_barrier();                            // prologue: tile 0 in LDS
     lds_barrier();                            // prologue: tile 0 decoded, tile 1 in LDS
     uint32_t next_o16[3] = {kInvalid, kInvalid, kInvalid};   // row offsets of the next tile to gather
