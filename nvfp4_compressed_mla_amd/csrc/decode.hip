@@ -537,9 +537,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       return (ok && pb != kInvalid && o * 16 + RB <= a.cache_bytes) ? (uint32_t)o : kInvalid;
     }
   };
-  // Source of byte pb of a row: the cache or the zero row.
+  // Source of byte pb of a row: the cache or the zero row. The two spellings give the same
+  // address, but the compiler's register schedule follows them: with pb added to both operands
+  // it hoists the zero-row pointer plus offset, and in the shared-rows instantiation the QK loop
+  // then reads every LDS operand into one register quad and waits for each read before its
+  // MFMA (34 serialized waits instead of 3; that kernel ran 40% slower). Selecting the base and
+  // adding pb afterwards keeps those reads in flight; the fused-append instantiation is the one
+  // measured faster with the other spelling.
   auto gather_src = [&](uint32_t o16, uint32_t pb) -> const uint8_t* {
-    return (o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 + pb : g_zero_row + pb;
+    if constexpr (AP) return (o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 + pb : g_zero_row + pb;
+    return ((o16 != kInvalid) ? a.cache + (int64_t)o16 * 16 : g_zero_row) + pb;
   };
   auto tile_offsets = [&](int tile, uint32_t (&o16)[3]) {
 #pragma unroll
