@@ -143,7 +143,13 @@ mla_status run_decode(mla::DecodeArgs a, int32_t H, bool dense, bool fp8, hipStr
     a.head_begin = part == 0 ? 0 : full * 64;
     a.n_hg = groups;
     a.total_items = T32 * groups * S;
-    a.items_per_xcd = (a.total_items + 7) / 8;
+    // Whole tokens per XCD (workgroup i runs on XCD i % 8) whenever that keeps the busiest XCD
+    // at the same number of rounds of its 32 compute units: the splits of a token then write
+    // their partials into one L2, and the merge reads them there (launch_combine deals tokens
+    // the same way). Otherwise an even split of the items.
+    const int32_t even = (a.total_items + 7) / 8;
+    const int32_t aligned = ((T32 + 7) / 8) * groups * S;
+    a.items_per_xcd = ((aligned + 31) / 32 == (even + 31) / 32) ? aligned : even;
     hipError_t e = mla::launch_decode(a, nh, dense, fp8, stream, part == first ? g_timing_start : nullptr,
                                       part == last ? g_timing_stop : nullptr);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");

@@ -1053,7 +1053,9 @@ hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream, hipEven
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
   const int32_t total = T * (H / 16) * 4;
-  const int32_t per_xcd = (total + 7) / 8;
+  // whole tokens per XCD, as the decode deals its splits, so that a token's partials are read
+  // from the L2 they were written to
+  const int32_t per_xcd = ((T + 7) / 8) * (H / 16) * 4;
   if (n_split <= 8)
     hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
                        n_split, ws_o, ws_lse, out, lse, per_xcd, total);
