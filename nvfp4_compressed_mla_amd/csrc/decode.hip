@@ -9,17 +9,19 @@
 //
 // MI355X design (not the page's Blackwell design). On gfx950 an MFMA and a VALU instruction of
 // the same wave do not overlap, while those of two waves sharing a SIMD do. The workgroup is
-// therefore split by role (per SIMD one math wave and two producer waves), and software-pipelined so that each
-// SIMD runs one wave's MFMAs while the other wave's VALU work issues:
+// therefore split by role (per SIMD one math wave and two producer waves), and software-pipelined
+// so that each SIMD runs one wave's MFMAs while the other wave's VALU work issues. Rows are
+// gathered 32 at a time into a 3-slot LDS ring with direct-to-LDS 16-byte loads, three tiles
+// ahead: the producers issue tiles 0..2 in the prologue, the math waves tile i+3 after the
+// softmax of tile i.
 //  * 4 math waves own one 16-head block each (up to 64 heads per workgroup). QK(i) runs
 //    v_mfma_f32_16x16x32_f16 with the decoded rows as the A operand and the block's queries
-//    (all 576 dims, FP16, in registers) as B, so each lane
-//    holds 8 rows of one head; then the online softmax (FP32, base 2, lazily moved running max)
-//    runs in registers and writes FP16 probabilities to LDS.
-//  * 8 producer waves (two per SIMD) gather rows 32 at a time into a 3-slot LDS ring with direct-to-LDS 16-byte
-//    loads (issued three tiles ahead), decode tile i+1 once into FP16 MFMA fragments (VALU, while
-//    the math waves run QK(i)), then run PV(i-1) on their 64 output dims for every head (MFMA,
-//    while the math waves run softmax(i)); V comes from the decoded tile through
+//    (all 576 dims, FP16, in registers) as B, so each lane holds 8 rows of one head; then the
+//    online softmax (FP32, base 2, lazily moved running max) runs in registers and writes FP16
+//    probabilities to LDS.
+//  * 8 producer waves (two per SIMD) decode tile i+1 once from the ring into FP16 MFMA fragments
+//    (VALU, while the math waves run QK(i)), then run PV(i-1) on their 64 output dims for every
+//    head (MFMA, while the math waves run softmax(i)); V comes from the decoded tile through
 //    ds_read_b64_tr_b16 transposing reads. Empty and out-of-range list entries never reach the
 //    ring: the index list is compacted up front, and padding rows read a zero row.
 // One barrier per 32-row tile; three decoded-tile buffers and two probability buffers.
