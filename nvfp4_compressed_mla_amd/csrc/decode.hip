@@ -910,34 +910,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
 }
 
-// Merge the n_split partial (o_s, lse_s) of each (token, head) in split order:
+// Merge the n_split partial (o_s, lse_s) of each (token, head):
 // M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
-// A thread owns two dims (16 apart) of 4 heads, the 16-byte FP16 unit the decode kernel stored.
-// SC > 0 handles up to SC splits with every load issued in one round (one memory latency);
-// SC == 0 handles any split count, 8 splits at a time.
+// A unit position is (token, 16-head block, pair of 16-dim blocks; a lane: two dims 16 apart of
+// 4 heads, the 16-byte FP16 unit the decode kernel stored). A workgroup has four waves: with
+// G = 1 they own four unit positions and merge all splits in split order; with G = 4 they own
+// one and take contiguous quarters of the splits, each merged in split order, then merged in
+// wave order (a fixed tree, so the result is deterministic) with wave g finalizing head e = g.
+// SCW > 0 handles up to SCW splits per wave with every load issued in one round; SCW == 0 any
+// count, 8 splits at a time.
 constexpr int kCombineChunk = 8;
 
-template <int SC>
+template <int SCW, int G>
 __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int32_t S,
-                                                      const _Float16* __restrict__ ws_o,
-                                                      const float* __restrict__ ws_lse,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse,
-                                                      int32_t per_xcd, int32_t total) {
-  // block = (token, 16-head block, 4 pairs of dim blocks); thread = (pair, lane)
+                                                         const _Float16* __restrict__ ws_o,
+                                                         const float* __restrict__ ws_lse,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ lse,
+                                                         int32_t per_xcd, int32_t total) {
+  __shared__ float4v xs[G > 1 ? G : 1][4][64];   // per wave: max, weight sum, acc0, acc1 (4 heads)
   const int hw = blockIdx.x;
   const int L = (hw & 7) * per_xcd + (hw >> 3);
   if (L >= total) return;
+  static_assert(G == 1 || G == 4, "one wave per unit position, or four sharing one");
   const int nhb = H >> 4;
-  const int tok = L / (nhb * 4);
-  const int r = L % (nhb * 4);
-  const int hb = r >> 2;
-  const int q = (r & 3) * 4 + (threadIdx.x >> 6);          // pair of dim blocks 2q, 2q + 1
-  const int lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
-  const int head = 16 * hb + 4 * kg;                      // heads head..head+3
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
+  // token, 16-head block, pair of dim blocks 2q, 2q + 1, share of the splits
+  const int tok = G == 1 ? L / (nhb * 4) : L / (nhb * 16);
+  const int r = G == 1 ? L % (nhb * 4) : L % (nhb * 16);
+  const int hb = G == 1 ? r >> 2 : r >> 4;
+  const int q = G == 1 ? (r & 3) * 4 + wv : r & 15;
+  const int g = G == 1 ? 0 : wv;
+  const int head = 16 * hb + 4 * kg;        // heads head..head+3
   const int64_t split_stride = (int64_t)H * kLatent;
   const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 16 + q) * 64 + lane) * 8;
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
+  const int per = (S + G - 1) / G;
+  const int s0 = min(g * per, S), s1 = min(s0 + per, S);   // this wave's splits
   const float4v ninf = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float4v M = ninf;
   float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0, wsum = acc0;
@@ -950,57 +959,86 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
       wsum[e] += wgt;
     }
   };
-  if constexpr (SC > 0) {
-    float4v ls[SC];
-    half8v ov[SC];
+  if constexpr (SCW > 0) {
+    float4v ls[SCW];
+    half8v ov[SCW];
 #pragma unroll
-    for (int j = 0; j < SC; ++j) {
-      const int s = min(j, S - 1);                        // splits past S: weight 0
-      ls[j] = (j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
+    for (int j = 0; j < SCW; ++j) {
+      const int s = min(s0 + j, S - 1);                   // splits past the share: weight 0
+      ls[j] = (s0 + j < s1) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
       ov[j] = *(const half8v*)(op + s * split_stride);
     }
 #pragma unroll
-    for (int j = 0; j < SC; ++j)
+    for (int j = 0; j < SCW; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], ls[j][e]);
 #pragma unroll
-    for (int j = 0; j < SC; ++j) merge(ls[j], ov[j]);
+    for (int j = 0; j < SCW; ++j) merge(ls[j], ov[j]);
   } else {
-    for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+    for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
       float4v v[kCombineChunk];
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j)
-        v[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)(s0 + j) * H) : ninf;
+        v[j] = (c0 + j < s1) ? *(const float4v*)(lp + (int64_t)(c0 + j) * H) : ninf;
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], v[j][e]);
     }
-    for (int s0 = 0; s0 < S; s0 += kCombineChunk) {
+    for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
       float4v ls[kCombineChunk];
       half8v ov[kCombineChunk];
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j) {
-        const int s = min(s0 + j, S - 1);
-        ls[j] = (s0 + j < S) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
+        const int s = min(c0 + j, s1 - 1);
+        ls[j] = (c0 + j < s1) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
         ov[j] = *(const half8v*)(op + s * split_stride);
       }
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j) merge(ls[j], ov[j]);
     }
   }
+  if constexpr (G == 1) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
+      float* o = out + ((int64_t)tok * H + head + e) * kLatent + 32 * q + l16;
+      o[0] = acc0[e] * inv;
+      o[16] = acc1[e] * inv;
+    }
+    if (lse && q == 0 && l16 == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lse[(int64_t)tok * H + head + e] =
+            (M[e] == -INFINITY) ? -INFINITY : M[e] + __builtin_amdgcn_logf(wsum[e]) * 0.69314718055994530942f;
+    }
+  } else {
+    xs[g][0][lane] = M;
+    xs[g][1][lane] = wsum;
+    xs[g][2][lane] = acc0;
+    xs[g][3][lane] = acc1;
+    __syncthreads();
+    // wave g finalizes head e = g over the four shares, in wave order
+    const int e = g;
+    float m = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < G; ++h) m = fmaxf(m, xs[h][0][lane][e]);
+    float ws = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mh = xs[h][0][lane][e];
+      const float f = (mh == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mh - m) * 1.4426950408889634f);
+      ws += f * xs[h][1][lane][e];
+      a0 += f * xs[h][2][lane][e];
+      a1 += f * xs[h][3][lane][e];
+    }
+    const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
     float* o = out + ((int64_t)tok * H + head + e) * kLatent + 32 * q + l16;
-    o[0] = acc0[e] * inv;
-    o[16] = acc1[e] * inv;
-  }
-  if (lse && q == 0 && l16 == 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
+    o[0] = a0 * inv;
+    o[16] = a1 * inv;
+    if (lse && q == 0 && l16 == 0)
       lse[(int64_t)tok * H + head + e] =
-          (M[e] == -INFINITY) ? -INFINITY : M[e] + __builtin_amdgcn_logf(wsum[e]) * 0.69314718055994530942f;
+          (m == -INFINITY) ? -INFINITY : m + __builtin_amdgcn_logf(ws) * 0.69314718055994530942f;
   }
 }
 
@@ -1054,19 +1092,21 @@ hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream, hipEven
 
 hipError_t launch_combine(int32_t T, int32_t H, int32_t n_split, const _Float16* ws_o,
                           const float* ws_lse, float* out, float* lse, hipStream_t stream) {
-  const int32_t total = T * (H / 16) * 4;
   // whole tokens per XCD, as the decode deals its splits, so that a token's partials are read
   // from the L2 they were written to
-  const int32_t per_xcd = ((T + 7) / 8) * (H / 16) * 4;
-  if (n_split <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
-                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
-  else if (n_split <= 16)
-    hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
-                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
-  else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, T, H,
-                       n_split, ws_o, ws_lse, out, lse, per_xcd, total);
+#define MLA_COMBINE(SCW, G)                                                                       \
+  do {                                                                                            \
+    const int32_t total = T * (H / 16) * 16 / (4 / (G));                                          \
+    const int32_t per_xcd = ((T + 7) / 8) * (H / 16) * 16 / (4 / (G));                            \
+    hipLaunchKernelGGL((combine_kernel<SCW, G>), dim3((unsigned)per_xcd * 8), dim3(256), 0, stream, \
+                       T, H, n_split, ws_o, ws_lse, out, lse, per_xcd, total);                    \
+  } while (0)
+  // up to 8 splits: one wave per unit position reads them all in one round (sharing them
+  // across waves measured slower there); more splits: four waves share them
+  if (n_split <= 8) MLA_COMBINE(8, 1);
+  else if (n_split <= 16) MLA_COMBINE(4, 4);
+  else MLA_COMBINE(0, 4);
+#undef MLA_COMBINE
   return hipGetLastError();
 }
 
