@@ -103,6 +103,25 @@ def test_split_invariance_and_determinism():
     th.assert_parity(outs[4][1], outs[4][2], ref_o, ref_l, what="split 8")
 
 
+@pytest.mark.parametrize("H,splits", [(16, 9), (16, 12), (64, 13), (16, 17), (80, 37)])
+def test_split_merge_with_shared_split_ranges(H, splits):
+    """Past 8 splits the merge's four waves each take a contiguous share of the splits (uneven
+    shares at 9, 13, 17; the 8-at-a-time loop past 16) and meet in LDS; the result matches one
+    split to the FP16 rounding of P, repeats bit for bit, and matches the oracle. H = 80 runs two
+    decode launches (64 + 16 heads) into one merge."""
+    print(f"case: split merge H={H} splits={splits}", flush=True)
+    case = th.build_case(2, 2, H, [6000, 3500], 2048, seed=70 + splits)
+    o1, l1 = _sparse(case, 1)
+    o, l = _sparse(case, splits)
+    rel = (o - o1).abs().amax() / o1.abs().amax()
+    assert rel < 1e-3, f"splits={splits} differs from 1 split by {rel}"
+    assert (l - l1).abs().amax() < 1e-4
+    o2, l2 = _sparse(case, splits)
+    assert torch.equal(o, o2) and torch.equal(l, l2), "not bitwise reproducible"
+    ref_o, ref_l = th.oracle_sparse(case)
+    th.assert_parity(o, l, ref_o, ref_l, what=f"H={H} splits={splits}")
+
+
 def test_permutation_and_duplicates():
     print("case: permuted list, duplicates", flush=True)
     case = th.build_case(1, 2, 16, [1500], 300, seed=91)
