@@ -71,6 +71,7 @@ def _separate(case, cache, lat, rope, slots, num_splits=0):
     (3, 16, [2000, 4100], 256, 1),
     (4, 32, [1500, 6000], 1024, 4),
     (15, 16, [1000, 2200], 256, 2),      # MTP-like: 15 new rows per request, 4 passes
+    (16, 32, [1100, 2300], 256, 3),      # the largest q_len the fused call takes
     (2, 80, [900, 2500], 256, 2),        # two decode launches (64 + 16 heads)
 ])
 def test_fused_append_equals_append_then_decode(q_len, H, ctx, topk, splits):
