@@ -118,15 +118,23 @@ __device__ void block_minmax(KeyAt key_at, int m, uint32_t& mn, uint32_t& mx, ui
 // match the resolved prefix into a 4096-bin LDS histogram (two buffers: the next one is cleared
 // while this one fills); thread t owns the B = 4096 / NT bins 4095 - B t - j (j < B), so a block
 // scan of their sums gives the number of keys above them.
-template <int NT, typename KeyAt>
+// REFINE: once the resolved bin holds at most 64 keys, they are gathered into LDS and one wave
+// ranks them exactly (each lane counts the keys above and equal to its own), which ends the
+// selection with the same threshold and count as further passes would. CLEARED: the caller
+// has zeroed the first histogram buffer and state[3] (and synchronized).
+template <int NT, bool REFINE = false, bool CLEARED = false, typename KeyAt>
 __device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi, int max_passes,
-                               uint32_t* hist /* LDS 2 x 4096 */, int* wsum, int* state, int& need) {
+                               uint32_t* hist /* LDS 2 x 4096 */, int* wsum, int* state /* LDS 4 */,
+                               int& need) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, mask = (hi >= 31) ? 0u : ~((2u << hi) - 1u);
   int rem = k;
   constexpr int B = kBins / NT;
-  for (int i = tid; i < kBins; i += NT) hist[i] = 0;
-  __syncthreads();
+  if constexpr (!CLEARED) {
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    if (tid == 0) state[3] = 0;
+    __syncthreads();
+  }
   for (int pass = 0; hi >= 0 && pass < max_passes; ++pass) {
     const int shift = max(hi - 11, 0);
     const uint32_t dmask = (2u << (hi - shift)) - 1u;
@@ -152,7 +160,11 @@ __device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi
     int run = block_excl_sum<NT>(sum, tot, wsum);
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      if (run < rem && run + c[j] >= rem) { state[0] = kBins - 1 - B * tid - j; state[1] = rem - run; }
+      if (run < rem && run + c[j] >= rem) {
+        state[0] = kBins - 1 - B * tid - j;
+        state[1] = rem - run;
+        state[2] = c[j];                                   // keys in the chosen bin
+      }
       run += c[j];
     }
     __syncthreads();
@@ -160,6 +172,37 @@ __device__ uint32_t select_kth(KeyAt key_at, int m, int k, uint32_t base, int hi
     mask |= dmask << shift;
     rem = state[1];
     hi = shift - 1;
+    if constexpr (REFINE) {
+      if (hi >= 0 && state[2] <= 64) {                     // workgroup-uniform
+        uint32_t* small = h_next;                          // cleared above, free until the next pass
+        for (int p0 = tid; p0 < m; p0 += 8 * NT) {
+          uint32_t dd[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int p = p0 + j * NT;
+            dd[j] = (p < m) ? key_at(p) - base : 0u;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (p0 + j * NT < m && (dd[j] & mask) == prefix) small[atomicAdd(&state[3], 1)] = dd[j];
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const int cnt = state[2];                        // == the entries gathered
+          const uint32_t x = (tid < cnt) ? small[tid] : 0u;
+          int gt = 0, eq = 0;
+          for (int j = 0; j < cnt; ++j) {
+            const uint32_t y = small[j];
+            gt += (y > x);
+            eq += (y == x);
+          }
+          if (tid < cnt && gt < rem && rem <= gt + eq) { state[0] = (int)x; state[1] = rem - gt; }
+        }
+        __syncthreads();
+        need = state[1];
+        return base + (uint32_t)state[0];
+      }
+    }
   }
   need = rem;
   return base + prefix;
@@ -172,7 +215,7 @@ __device__ uint32_t select_kth_lds(KeyAt key_at, int m, int k, uint32_t* hist, i
   uint32_t mn, mx;
   block_minmax<NT>(key_at, m, mn, mx, red);
   if (mn == mx) { need = k; return mx; }
-  return select_kth<NT>(key_at, m, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
+  return select_kth<NT, true>(key_at, m, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
 }
 
 // Emit, in list order, the entries of key_at(0 .. m-1) above thr plus the first `need` equal to
@@ -266,7 +309,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   __shared__ uint32_t skeys[kTopkSample];
   __shared__ uint32_t hist[2 * kBins];
   __shared__ int wsum[kFilterThreads / 64];
-  __shared__ int state[2];
+  __shared__ int state[4];
   const int tok = blockIdx.x / n_slices, g = blockIdx.x - tok * n_slices;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t seg = ((int64_t)tok * n_slices + g) * kSegsPerSlice + w;
@@ -344,7 +387,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   __shared__ uint32_t keys[kTopkCandCap];
   __shared__ int32_t pos[kTopkCandCap];
   __shared__ uint32_t hist[2 * kBins];
-  __shared__ int state[2];
+  __shared__ int state[4];
   constexpr int NT = kMergeThreads, W = NT / 64;
   __shared__ int wsum[W];
   __shared__ uint32_t red[2 * W];
@@ -414,27 +457,49 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     __syncthreads();
     const int total = soff[n_seg];
     if (!fallback_s) {
-      // the lists into LDS in position order (segment by segment)
+      // the lists into LDS in position order (segment by segment), with the smallest and
+      // largest key and the selection's first histogram cleared in the same phase
       int longest = 0;
+      uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
 #pragma unroll
       for (int u = 0; u < kSegPerWave; ++u) {
         const int sg = min(w + W * u, n_seg);
         const int o = soff[sg], c = soff[min(sg + 1, n_seg)] - o;
         longest = max(longest, c);
-        if (lane < c && o + lane < kTopkCandCap) { keys[o + lane] = kv[u]; pos[o + lane] = pv[u]; }
+        if (lane < c && o + lane < kTopkCandCap) {
+          keys[o + lane] = kv[u];
+          pos[o + lane] = pv[u];
+          lmn = min(lmn, kv[u]);
+          lmx = max(lmx, kv[u]);
+        }
       }
       if (longest > 64) {                                    // entries 64.. of longer segments (rare)
         for (int sg = w; sg < n_seg; sg += W) {
           const int o = soff[sg], c = soff[sg + 1] - o;
           for (int e = 64 + lane; e < c && o + e < kTopkCandCap; e += 64) {
             const int64_t at = (sbase + sg) * cap_seg + e;
-            keys[o + e] = cand_key[at];
+            const uint32_t kk = cand_key[at];
+            keys[o + e] = kk;
             pos[o + e] = cand_pos[at];
+            lmn = min(lmn, kk);
+            lmx = max(lmx, kk);
           }
         }
       }
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+      if (tid == 0) state[3] = 0;
+      lmn = wave_scan(lmn, 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return min(x, y); });
+      lmx = wave_scan(lmx, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
+      if (lane == 63) { red[w] = lmn; red[W + w] = lmx; }
       __syncthreads();
-      const uint32_t thr = (total > k) ? select_kth_lds<NT>(lds_key, total, k, hist, wsum, state, red, need) : 0u;
+      uint32_t mn = red[0], mx = red[W];
+#pragma unroll
+      for (int v = 1; v < W; ++v) { mn = min(mn, red[v]); mx = max(mx, red[W + v]); }
+      uint32_t thr = 0u;                                     // 0 (total <= k): every entry
+      if (total > k) {
+        if (mn == mx) { need = k; thr = mx; }
+        else thr = select_kth<NT, true, true>(lds_key, total, k, mn, 31 - __builtin_clz(mx - mn), 3, hist, wsum, state, need);
+      }
       ordered_emit<NT>(lds_key, total, thr, need, cnt, [&](int i) { return pos[i]; }, to_out);
     } else {
       // the whole row from memory (exact whatever the sample did)
