@@ -21,9 +21,9 @@
 // request: wave w scores tokens w, w+8, ... Per token the wave holds the queries of the 64 heads
 // as four A operands (32 VGPRs) and runs v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit
 // block scales, FP32 accumulation: the whole 128-dim dot product in one instruction) over
-// 16-position tiles, two tiles (8 independent MFMAs) at a time: a lane then holds 4 heads of one
-// position per MFMA, applies the ReLU and the head weights, and the four lane groups are summed
-// with lane swaps. Products of two E4M3 values
+// 16-position tiles, four tiles at a time: a lane holds 4 heads of one position per MFMA and
+// applies the ReLU and the head weights; lane swaps then sum the four lane groups so that lane
+// group g ends with the whole score of tile g, and every lane stores one position. Products of two E4M3 values
 // are exact in FP32, so the only rounding is the FP32 accumulation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,13 +40,6 @@ constexpr int kIdxThreads = 512;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxBlockRows = 512;                      // positions per workgroup, at most
 constexpr int kIdxScaleOff = kPageRows * kIndexerDim;   // 8192: scales after the keys
-
-__device__ __forceinline__ float idx_group4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 __device__ __forceinline__ float idx_relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.4028234663852886e38f); }
 
@@ -95,7 +88,11 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerAr
   __syncthreads();
 
   // ---- score: wave w takes query tokens w, w+8, ... ------------------------------------------
-  for (int t = w; t < a.q_len; t += kIdxWaves) {
+  // The wave index goes through a scalar register, so that everything per token is known to be
+  // wave-uniform: the output's buffer resource then lives in scalar registers (a resource in
+  // vector registers costs a compare-and-branch loop around every store).
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  for (int t = wu; t < a.q_len; t += kIdxWaves) {
     const int64_t tok = (int64_t)b * a.q_len + t;
     const int vis = min(a.seq_lens[b] - a.q_len + 1 + t, n_pos);   // positions 0 .. vis-1
     const int nr = min(vis - p0, a.block_rows);
@@ -116,42 +113,53 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerAr
     const __amdgpu_buffer_rsrc_t out_rs =
         __builtin_amdgcn_make_buffer_rsrc(a.scores + tok * a.n_max + p0, (short)0, nr * 4, 0x00020000);
     const int n_kt = (nr + 15) >> 4;
-    // The key rows a lane reads step by 16, so their swizzle (row & 7 = l16 & 7) is fixed.
+    // Lane l16 reads row l16 of every tile; rows step by 16, so the swizzle (row & 7 = l16 & 7)
+    // is fixed.
+    const uint8_t* kr0 = keys + l16 * kIndexerDim;
     const int koff0 = ((2 * kg) ^ (l16 & 7)) << 4, koff1 = ((2 * kg + 1) ^ (l16 & 7)) << 4;
-    // two 16-position tiles per step: 8 independent MFMAs, then their epilogues
-    for (int kt0 = 0; kt0 < n_kt; kt0 += 2) {
-      f32x4 d[2][4];
-      int rr[2];
+    // Four 16-position tiles per step. n_kt <= 32, so tiles kt0 .. kt0 + 3 (kt0 < n_kt, a
+    // multiple of 4) stay inside the 512 staged rows; rows past the block's end hold zeros and
+    // their sums are not stored.
+    auto kfrag = [&](int tile) -> i32x8 {
+      const uint8_t* kr = kr0 + tile * 16 * kIndexerDim;
+      const uint4 k0 = *(const uint4*)(kr + koff0);
+      const uint4 k1 = *(const uint4*)(kr + koff1);
+      return i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+    };
+    i32x8 kn = kfrag(0);
+    for (int kt0 = 0; kt0 < n_kt; kt0 += 4) {
+      float part[4];                           // this lane group's 16 heads, tile kt0 + u
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // a tile past n_kt (not stored) reads the last row's bytes at this lane's offsets
-        rr[u] = min((kt0 + u) * 16 + l16, kIdxBlockRows - 1);
-        const uint8_t* kr = keys + rr[u] * kIndexerDim;
-        const uint4 k0 = *(const uint4*)(kr + koff0);
-        const uint4 k1 = *(const uint4*)(kr + koff1);
-        const i32x8 kb = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+      for (int u = 0; u < 4; ++u) {
+        const i32x8 kb = kn;
+        kn = kfrag(min(kt0 + u + 1, 31));      // the next tile's keys, read under this tile's work
+        f32x4 d[4];
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
           // E4M3 x E4M3 (format 0 for both operands), E8M0 block scales 127 = 1.0
-          d[u][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          d[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               qa[hb], kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
         // ReLU as one v_med3_f32 (fmaxf would add a NaN-canonicalising max: the dot products are
-        // sums of exact products of finite E4M3 values, never NaN)
-        float sh[4];
+        // sums of exact products of finite E4M3 values, never NaN); one weighted chain
+        float s = wv[0][0] * idx_relu(d[0][0]);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          sh[hb] = wv[hb][0] * idx_relu(d[u][hb][0]);
+        for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-          for (int e = 1; e < 4; ++e) sh[hb] = __builtin_fmaf(wv[hb][e], idx_relu(d[u][hb][e]), sh[hb]);
-        }
-        const float s = idx_group4_sum((sh[0] + sh[1]) + (sh[2] + sh[3])) * kscale[rr[u]];
-        const int r = (kt0 + u) * 16 + l16;
-        // one lane group stores (the others hold the same sum); offsets past the row are dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), out_rs, kg == 0 ? 4 * r : 0x7FFFFFF0, 0, 0);
+          for (int e = (hb == 0 ? 1 : 0); e < 4; ++e) s = __builtin_fmaf(wv[hb][e], idx_relu(d[hb][e]), s);
+        part[u] = s;
       }
+      // Reduce-scatter over the four lane groups: the 32-lane swaps pair groups g and g + 2
+      // (the lower half keeps tiles 0 and 1, the upper half tiles 2 and 3), the 16-lane swap
+      // pairs g and g + 1, so lane group kg ends with the whole sum of tile kt0 + kg.
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float r0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float r1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(r0), __float_as_uint(r1), false, false);
+      const int r = (kt0 + kg) * 16 + l16;
+      const float s = (__uint_as_float(z[0]) + __uint_as_float(z[1])) * kscale[r];
+      // every lane stores its own position; offsets past the row are dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), out_rs, 4 * r, 0, 0);
     }
   }
 }
