@@ -41,7 +41,12 @@ constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxBlockRows = 512;                      // positions per workgroup, at most
 constexpr int kIdxScaleOff = kPageRows * kIndexerDim;   // 8192: scales after the keys
 
-__device__ __forceinline__ float idx_relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.4028234663852886e38f); }
+// ReLU on the bits: a negative float (-0.0 included) has the sign bit set and so is a negative
+// int, which the max replaces by 0 (= +0.0f); a positive float is a positive int and passes
+// unchanged. One v_max_i32 with an inline 0 (a float max would add a NaN-canonicalising max, and a
+// v_med3_f32 needs FLT_MAX in a register); exact here because the dot products are sums of exact
+// products of finite E4M3 values, never NaN.
+__device__ __forceinline__ float idx_relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerArgs a) {
   // key r, 16-byte piece c (dims 16c..16c+15) at r*128 + 16*(c ^ (r & 7))
@@ -139,8 +144,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_kernel(const IndexerAr
           // E4M3 x E4M3 (format 0 for both operands), E8M0 block scales 127 = 1.0
           d[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               qa[hb], kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-        // ReLU as one v_med3_f32 (fmaxf would add a NaN-canonicalising max: the dot products are
-        // sums of exact products of finite E4M3 values, never NaN); one weighted chain
+        // ReLU and head weights: one weighted chain over the lane's 16 heads
         float s = wv[0][0] * idx_relu(d[0][0]);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
