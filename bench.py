@@ -442,7 +442,7 @@ def indexer_chain(dev, reps=20, rot=4):
     res["indexer_mfma_frac_fp8"] = round(flops / t_idx / 5.0e15, 4)
     res["indexer_GBps"] = round(byt / t_idx / 1e9, 1)
     res["indexer_hbm_frac"] = round(byt / t_idx / 8e12, 4)
-    res["note"] = ("indexer: 64 heads x 128 dims E4M3, MFMA-bound (36.7 GFLOP, 28.8 MB per launch); "
+    res["note"] = ("indexer: 64 heads x 128 dims E4M3, a dense contraction (36.7 GFLOP, 28.8 MB per launch); "
                    "chain: indexer + top-k + decode captured together per step")
     del wk, ix, scores
     torch.cuda.empty_cache()
