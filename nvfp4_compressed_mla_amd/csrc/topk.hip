@@ -302,6 +302,16 @@ __device__ __forceinline__ int sample_pos(int i, int n) {
   return (int)(((int64_t)(i >> 3) * n) / kTopkSampleRuns) + (i & 7);
 }
 
+// A wave-uniform pointer, rebuilt from scalar reads of its halves: a buffer resource made from
+// it stays in scalar registers even where the compiler cannot prove the pointer uniform (a
+// resource in vector registers costs a compare-and-branch loop around every access).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t n_max, const int32_t* __restrict__ seq_lens,
     int32_t q_len, int32_t k, int64_t slice, int32_t n_slices, int32_t cap_seg,
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   __shared__ int wsum[kFilterThreads / 64];
   __shared__ int state[4];
   const int tok = blockIdx.x / n_slices, g = blockIdx.x - tok * n_slices;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index through a scalar register: the segment, its positions and its buffer
+  // resources are then known to be wave-uniform (a resource in vector registers costs a
+  // compare-and-branch loop around every access)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t seg = ((int64_t)tok * n_slices + g) * kSegsPerSlice + w;
   const float* row = scores + (int64_t)tok * n_max;
   // this wave's segment of the slice, in batches of kFilterUnroll rows of 64 positions; the
@@ -319,13 +332,22 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   // and stays in flight while the cut is found
   const int64_t seg_len = slice / kSegsPerSlice;
   const int64_t p_begin = (int64_t)g * slice + w * seg_len;
-  // Branch-free loads: positions at or past `lim` re-read entry lim - 1 (lim >= 1); their values
-  // are never selected, since the selection tests the position against the row's end.
+  // A batch wholly before `lim` is read through a buffer resource over exactly its 64 x
+  // kFilterUnroll entries (one load per entry with a constant lane offset, no address arithmetic;
+  // every access is inside the resource); a batch that crosses `lim` re-reads entry lim - 1
+  // (lim >= 1) for its positions at or past it, whose values are never selected (the selection
+  // tests the position against the row's end).
+  constexpr int64_t kBatch = 64 * kFilterUnroll;
   auto load_batch = [&](int64_t b0, int64_t lim, float (&v)[kFilterUnroll]) {
+    if (b0 + kBatch <= lim) {                              // wave-uniform
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(row + b0), (short)0, (int)(4 * kBatch), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < kFilterUnroll; ++j) {
-      const int64_t p = b0 + j * 64 + lane;
-      v[j] = row[min(p, lim - 1)];
+      for (int j = 0; j < kFilterUnroll; ++j)
+        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 256 * j, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < kFilterUnroll; ++j) v[j] = row[min(b0 + j * 64 + lane, lim - 1)];
     }
   };
   float cur[kFilterUnroll];
@@ -347,34 +369,50 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   int unused;
   const uint32_t cut = select_kth<kFilterThreads>([&](int i) { return skeys[i]; }, kTopkSample, sample_rank(k, n),
                                   0u, 31, 2, hist, wsum, state, unused);
-  uint32_t* ck = cand_key + seg * cap_seg;
-  int32_t* cp = cand_pos + seg * cap_seg;
+  // The segment's list through buffer resources of cap_seg entries (stores past the capacity are
+  // skipped, while cnt keeps the true count).
+  const __amdgpu_buffer_rsrc_t ck_rs =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(cand_key + seg * cap_seg), (short)0, 4 * cap_seg, 0x00020000);
+  const __amdgpu_buffer_rsrc_t cp_rs =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(cand_pos + seg * cap_seg), (short)0, 4 * cap_seg, 0x00020000);
   int cnt = 0;
-  auto take_batch = [&](int64_t b0, const float (&v)[kFilterUnroll]) {
+  // A cut at or above +0 (key >= 2^31): key(u) >= cut exactly when the score's bits, read as a
+  // signed int, are >= cut - 2^31 (a negative score, -0 included, is a negative int and never
+  // reaches it; a non-negative score's key is its bits plus 2^31). One compare per entry then,
+  // and the key is formed only for the entries stored.
+  const bool cut_nonneg = cut >= 0x80000000u;
+  const int cut_bits = (int)(cut & 0x7FFFFFFFu);
+  auto take_batch = [&](auto fast_tag, int64_t b0, const float (&v)[kFilterUnroll]) {
+    constexpr bool FAST = decltype(fast_tag)::value;     // whole batch in range, cut >= +0
+    const int rem = (int)min<int64_t>(p_end - b0, kBatch);
 #pragma unroll
     for (int j = 0; j < kFilterUnroll; ++j) {
-      const int64_t p = b0 + j * 64 + lane;
-      const uint32_t key = score_key(v[j]);
-      const bool sel = p < p_end && key >= cut;
+      const bool sel = FAST ? __float_as_int(v[j]) >= cut_bits : (j * 64 + lane < rem && score_key(v[j]) >= cut);
       const uint64_t mask = __ballot(sel);
       if (sel) {
         const int at = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (at < cap_seg) { ck[at] = key; cp[at] = (int32_t)p; }
+        if (at < cap_seg) {
+          __builtin_amdgcn_raw_buffer_store_b32(score_key(v[j]), ck_rs, 4 * at, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(b0 + j * 64 + lane), cp_rs, 4 * at, 0, 0);
+        }
       }
       cnt += __popcll(mask);
     }
   };
+  auto take = [&](int64_t b0, const float (&v)[kFilterUnroll]) {
+    if (cut_nonneg && b0 + kBatch <= p_end) take_batch(std::true_type{}, b0, v);    // workgroup-uniform
+    else take_batch(std::false_type{}, b0, v);
+  };
   // Two register buffers used in turn (no copy between them, which would wait for the batch
   // just issued): while one batch is taken, the next one is in flight.
-  constexpr int64_t kBatch = 64 * kFilterUnroll;
   float nxt[kFilterUnroll];
   for (int64_t b0 = p_begin; b0 < p_end; b0 += 2 * kBatch) {
     if (b0 + kBatch < p_end) load_batch(b0 + kBatch, p_end, nxt);
-    take_batch(b0, cur);
+    take(b0, cur);
     if (b0 + kBatch >= p_end) break;
     if (b0 + 2 * kBatch < p_end) load_batch(b0 + 2 * kBatch, p_end, cur);
-    take_batch(b0 + kBatch, nxt);
+    take(b0 + kBatch, nxt);
   }
   if (lane == 0) seg_cnt[seg] = cnt;                       // the true count, even past cap_seg
 }

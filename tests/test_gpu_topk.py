@@ -63,6 +63,19 @@ def test_topk_all_equal_and_signed_zeros():
     assert np.array_equal(got, tk.topk_indices(s, [40000], 2, 1000))
 
 
+
+def test_topk_negative_threshold():
+    """Every score negative, so the k-th largest key is below the key of +0: the stream takes its
+    general comparison (the one-compare form needs a threshold at or above +0). Row 1's 12,000
+    largest scores are -0.0, more than k: ties by position, through the fallback."""
+    print("case: topk negative threshold", flush=True)
+    rng = np.random.default_rng(77)
+    s = (-np.abs(rng.standard_normal((2, 1, 60000))) - 0.5).astype(np.float32)
+    s[1, 0, ::5] = -0.0
+    got = _run(s, [60000, 60000], 1, 2048)
+    assert np.array_equal(got, tk.topk_indices(s, [60000, 60000], 1, 2048))
+    assert list(got[1, 0]) == list(range(0, 5 * 2048, 5))
+
 def _sample_positions(n):
     # the 2048 positions the cut is drawn from: 256 evenly spaced runs of 8
     return np.array([(i >> 3) * n // 256 + (i & 7) for i in range(2048)])
