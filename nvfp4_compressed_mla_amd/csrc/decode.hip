@@ -897,12 +897,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int head = 16 * hbg + 4 * kg + e;
-          const float lse_v = ll[e] > 0.0f
-              ? (mm[e] + __builtin_amdgcn_logf(ll[e])) * 0.69314718055994530942f : -INFINITY;
+          // log2 units (the max is kept in them); the split merge weighs in log2 units too, so
+          // only the final value is scaled to the natural log
+          const float lse2 = ll[e] > 0.0f ? mm[e] + __builtin_amdgcn_logf(ll[e]) : -INFINITY;
           if (final_out) {
-            if (a.lse) a.lse[otok * a.H + head] = lse_v;
+            if (a.lse) a.lse[otok * a.H + head] = lse2 * 0.69314718055994530942f;
           } else {
-            a.ws_lse[(otok * a.n_split + split) * a.H + head] = lse_v;
+            a.ws_lse[(otok * a.n_split + split) * a.H + head] = lse2;
           }
         }
       }
@@ -910,8 +911,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
 }
 
-// Merge the n_split partial (o_s, lse_s) of each (token, head):
-// M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s, lse = M + log(sum w_s).
+// Merge the n_split partial (o_s, lse_s) of each (token, head), with lse_s in log2 units as the
+// decode writes them: M = max lse_s, w_s = 2^(lse_s - M), o = sum w_s o_s / sum w_s, and the
+// natural-log lse = (M + log2(sum w_s)) ln 2.
 // A unit position is (token, 16-head block, pair of 16-dim blocks; a lane: two dims 16 apart of
 // 4 heads, the 16-byte FP16 unit the decode kernel stored). A workgroup has four waves: with
 // G = 1 they own four unit positions and merge all splits in split order; with G = 4 they own
@@ -934,7 +936,10 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   if (L >= total) return;
   static_assert(G == 1 || G == 4, "one wave per unit position, or four sharing one");
   const int nhb = H >> 4;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 4, l16 = lane & 15;
+  // the wave index through a scalar register: the split share and the per-split bases below are
+  // then wave-uniform (scalar base plus a 32-bit lane offset per load)
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, kg = lane >> 4,
+            l16 = lane & 15;
   // token, 16-head block, pair of dim blocks 2q, 2q + 1, share of the splits
   const int tok = G == 1 ? L / (nhb * 4) : L / (nhb * 16);
   const int r = G == 1 ? L % (nhb * 4) : L % (nhb * 16);
@@ -943,17 +948,26 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   const int g = G == 1 ? 0 : wv;
   const int head = 16 * hb + 4 * kg;        // heads head..head+3
   const int64_t split_stride = (int64_t)H * kLatent;
-  const _Float16* op = ws_o + (int64_t)tok * S * split_stride + ((int64_t)(hb * 16 + q) * 64 + lane) * 8;
+  const _Float16* tok_o = ws_o + (int64_t)tok * S * split_stride;   // the token's partials
+  const int o_lane = ((hb * 16 + q) * 64 + lane) * 8;                  // within one split's H x 512
   const float* lp = ws_lse + (int64_t)tok * S * H + head;
+  auto o_at = [&](int s) { return *(const half8v*)(tok_o + (int64_t)s * split_stride + o_lane); };
   const int per = (S + G - 1) / G;
   const int s0 = min(g * per, S), s1 = min(s0 + per, S);   // this wave's splits
   const float4v ninf = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float4v M = ninf;
   float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0, wsum = acc0;
+  // Weights against the running max; a head with no valid row in any split (max -inf) takes 0
+  // as its reference, so that every weight is exp2(-inf) = 0 without a test per split.
+  float4v Mb;
+  auto set_ref = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Mb[e] = (M[e] == -INFINITY) ? 0.0f : M[e];
+  };
   auto merge = [&](const float4v& ls, const half8v& hv) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float wgt = (ls[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((ls[e] - M[e]) * 1.4426950408889634f);
+      const float wgt = __builtin_amdgcn_exp2f(ls[e] - Mb[e]);
       acc0[e] += wgt * (float)hv[e];
       acc1[e] += wgt * (float)hv[4 + e];
       wsum[e] += wgt;
@@ -966,12 +980,13 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
     for (int j = 0; j < SCW; ++j) {
       const int s = min(s0 + j, S - 1);                   // splits past the share: weight 0
       ls[j] = (s0 + j < s1) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
-      ov[j] = *(const half8v*)(op + s * split_stride);
+      ov[j] = o_at(s);
     }
 #pragma unroll
     for (int j = 0; j < SCW; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], ls[j][e]);
+    set_ref();
 #pragma unroll
     for (int j = 0; j < SCW; ++j) merge(ls[j], ov[j]);
   } else {
@@ -985,6 +1000,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
 #pragma unroll
         for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], v[j][e]);
     }
+    set_ref();
     for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
       float4v ls[kCombineChunk];
       half8v ov[kCombineChunk];
@@ -992,7 +1008,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
       for (int j = 0; j < kCombineChunk; ++j) {
         const int s = min(c0 + j, s1 - 1);
         ls[j] = (c0 + j < s1) ? *(const float4v*)(lp + (int64_t)s * H) : ninf;
-        ov[j] = *(const half8v*)(op + s * split_stride);
+        ov[j] = o_at(s);
       }
 #pragma unroll
       for (int j = 0; j < kCombineChunk; ++j) merge(ls[j], ov[j]);
@@ -1001,7 +1017,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
   if constexpr (G == 1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
+      // v_rcp_f32 (1 ulp): the weight sum is >= 1 when it is not 0 (the max split weighs 1)
+      const float inv = wsum[e] > 0.0f ? __builtin_amdgcn_rcpf(wsum[e]) : 0.0f;
       float* o = out + ((int64_t)tok * H + head + e) * kLatent + 32 * q + l16;
       o[0] = acc0[e] * inv;
       o[16] = acc1[e] * inv;
@@ -1010,7 +1027,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         lse[(int64_t)tok * H + head + e] =
-            (M[e] == -INFINITY) ? -INFINITY : M[e] + __builtin_amdgcn_logf(wsum[e]) * 0.69314718055994530942f;
+            (M[e] == -INFINITY) ? -INFINITY : (M[e] + __builtin_amdgcn_logf(wsum[e])) * 0.69314718055994530942f;
     }
   } else {
     xs[g][0][lane] = M;
@@ -1027,18 +1044,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int32_t T, int32_t H, int3
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mh = xs[h][0][lane][e];
-      const float f = (mh == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mh - m) * 1.4426950408889634f);
+      const float f = (mh == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mh - m);
       ws += f * xs[h][1][lane][e];
       a0 += f * xs[h][2][lane][e];
       a1 += f * xs[h][3][lane][e];
     }
-    const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
+    const float inv = ws > 0.0f ? __builtin_amdgcn_rcpf(ws) : 0.0f;           // as above: ws >= 1
     float* o = out + ((int64_t)tok * H + head + e) * kLatent + 32 * q + l16;
     o[0] = a0 * inv;
     o[16] = a1 * inv;
     if (lse && q == 0 && l16 == 0)
       lse[(int64_t)tok * H + head + e] =
-          (m == -INFINITY) ? -INFINITY : m + __builtin_amdgcn_logf(ws) * 0.69314718055994530942f;
+          (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(ws)) * 0.69314718055994530942f;
   }
 }
 

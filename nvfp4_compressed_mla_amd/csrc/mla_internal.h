@@ -31,7 +31,7 @@ struct DecodeArgs {
   float* out;               // [T, H, 512] (n_split == 1)
   float* lse;               // [T, H] or null (n_split == 1)
   _Float16* ws_o;           // [T, n_split, H/16, 16, 64, 2, 4] FP16 partial outputs (n_split > 1)
-  float* ws_lse;            // [T, n_split, H] partial log-sum-exp (natural log)
+  float* ws_lse;            // [T, n_split, H] partial log-sum-exp (log2 units)
   // Shared-row mode (the rows selected by a group of up to 4 consecutive query tokens of one
   // request, deduplicated): workgroup = (group, 16-head block, split), head block u of the
   // workgroup = token 4g+u of the group.
