@@ -658,24 +658,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           const float m_new = move ? mx : m_run;
           const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
           half4v pf[2];
-          float psum = 0.0f;
           if (full) {
   #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
-              pf[e >> 2][e & 3] = pv;
-              psum += (float)pv;
-            }
+            for (int e = 0; e < 8; ++e) pf[e >> 2][e & 3] = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
           } else {
   #pragma unroll
             for (int e = 0; e < 8; ++e) {
               // a masked row is 0 (also while no valid row has been seen: m_new = -inf)
-              const _Float16 pv = (sv[e] == -INFINITY) ? (_Float16)0.0f
+              pf[e >> 2][e & 3] = (sv[e] == -INFINITY) ? (_Float16)0.0f
                                                        : (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
-              pf[e >> 2][e & 3] = pv;
-              psum += (float)pv;
             }
           }
+          // the row sum of the FP16 probabilities PV uses, in FP32: v_dot2_f32_f16 against (1, 1)
+          // adds two of them per instruction (the products are exact)
+          const half2v one2 = half2v{(_Float16)1.0f, (_Float16)1.0f};
+          float psum = 0.0f;
+  #pragma unroll
+          for (int h = 0; h < 4; ++h)
+            psum = __builtin_amdgcn_fdot2(half2v{pf[h >> 1][2 * (h & 1)], pf[h >> 1][2 * (h & 1) + 1]}, one2, psum, false);
           l_run = l_run * alpha + psum;
           m_run = m_new;
           const int ph = 16 * w + l16;
