@@ -65,3 +65,32 @@ def test_decode_kernels_keep_lds_reads_in_flight(decode_asm):
         if serialized > MAX_SERIALIZED_WAITS or scratch or vgpr > 168:
             bad.append((name, serialized, scratch, vgpr))
     assert not bad, f"(kernel, lgkmcnt(0)->mfma waits, scratch ops, vgprs): {bad}"
+
+
+def _compile(tmp_path_factory, name):
+    out = tmp_path_factory.mktemp("asm_" + name) / (name + ".s")
+    flags = [f for f in B.FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [B.HIPCC, *flags, "-I", os.path.join(B.ROOT, "include"), "-I", B.CSRC, "-S",
+           "--cuda-device-only", os.path.join(B.CSRC, name + ".hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text()
+
+
+@pytest.mark.parametrize("name", ["codec", "decode", "fp8", "indexer", "layout", "topk", "union"])
+def test_no_waterfall_loops_and_no_scratch(tmp_path_factory, name):
+    """A buffer resource or scalar operand the compiler cannot prove wave-uniform is rebuilt around
+    every access in a loop of readfirstlane + 64-bit compare + exec mask (the indexer's score
+    stores and the top-k filter's list stores once spent most of their time there). Every kernel
+    keeps such values in scalar registers, and none spills to scratch."""
+    if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    asm = _compile(tmp_path_factory, name)
+    lines = [l.split(";")[0].strip() for l in asm.split("\n")]
+    waterfalls = sum(1 for i in range(len(lines) - 6)
+                     if lines[i].startswith("v_readfirstlane_b32")
+                     and any(x.startswith("v_cmp_eq_u64") for x in lines[i:i + 8])
+                     and any(x.startswith("s_and_saveexec_b64") for x in lines[i:i + 10]))
+    scratch = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", asm)
+    assert waterfalls == 0, f"{name}.hip: {waterfalls} waterfall loops"
+    assert scratch and all(int(s) == 0 for s in scratch), f"{name}.hip: scratch {scratch}"
